@@ -1,0 +1,178 @@
+/*
+ * router.h -- C ABI of the MI355X (gfx950) fused MoE router library.
+ *
+ * The library implements the two fused router operations of "[Common]
+ * Optimize fused router forward/backward kernels" (NVIDIA TransformerEngine
+ * pull request 3012, "Summary"): fused_topk_with_score_function and
+ * fused_score_for_moe_aux_loss, each with a forward and a backward, as
+ * hand-written HIP kernels.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.   Every [T,E] array is row-major and contiguous: element (t, j)
+ *           sits at offset t*E + j.  T = tokens, E = experts, K = top-k.
+ * Memory.   All array arguments are DEVICE pointers, allocated by the
+ *           caller.  The library allocates, frees and retains nothing.
+ *           Every output element is written, so outputs may be
+ *           uninitialised.  Inputs are read only.  Outputs must not alias
+ *           inputs.  Each array must be aligned to its element size (else
+ *           ROUTER_ERR_INVALID_ARG); when every array is 16-byte aligned
+ *           and E is a multiple of 4 the kernels use vector loads and
+ *           stores, otherwise element-wise ones (same results).
+ * Dtypes.   `dtype` (router_dtype) is the storage type of logits, probs,
+ *           scores and gradients.  intermediate is always fp32 and the
+ *           routing map is one byte per element holding 0 or 1 (a torch
+ *           bool tensor).  expert_bias is fp32.  Arithmetic is fp32.
+ * Ordering. Work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ *           null stream) and is asynchronous: a return of ROUTER_OK means
+ *           the kernels were launched.  No host synchronisation and no
+ *           host<->device copy happens inside a call.
+ * Errors.   All arguments are checked on the host before anything is
+ *           launched; on any error nothing is written and the status is
+ *           returned.  There is no abort and no device assert.  T == 0 is a
+ *           valid no-op.  Finite logits are a precondition.
+ * Threads.  Calls are reentrant; the only state is a per-device cache of
+ *           device attributes and the top-k path threshold.
+ */
+#ifndef SCORE_FUNCTION_TOP_AMD_ROUTER_H
+#define SCORE_FUNCTION_TOP_AMD_ROUTER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ROUTER_OK = 0,
+    ROUTER_ERR_INVALID_ARG = 1, /* argument outside the operation's domain */
+    ROUTER_ERR_OVERFLOW = 2,    /* T*E*element size overflows 64 bits      */
+    ROUTER_ERR_UNSUPPORTED = 3, /* valid, but not implemented (E > 4096,
+                                   expert bias with softmax)             */
+    ROUTER_ERR_HIP = 4          /* a HIP call or kernel launch failed      */
+} router_status;
+
+typedef enum { ROUTER_F32 = 0, ROUTER_BF16 = 1 } router_dtype;
+
+typedef enum { ROUTER_SOFTMAX = 0, ROUTER_SIGMOID = 1 } router_score_fn;
+
+/* Largest number of experts the kernels handle. */
+#define ROUTER_MAX_EXPERTS 4096
+
+/*
+ * router_topk_fwd -- fused_topk_with_score_function forward.
+ * Passage: the fused-router page, "Performance" paragraph (the forward
+ * reads logits [T,E] and writes probs [T,E] in the logits dtype, a one-byte
+ * routing_map [T,E] and a four-byte intermediate [T,E]) and "Hardening"
+ * (1 <= topk <= E; topk divisible by group_topk).
+ *
+ * Per token (row of E logits x):
+ *   s      = softmax(x) over all E, or sigmoid(x) element-wise (score_fn).
+ *   key    = x without expert_bias; fp32(s + expert_bias) with it.
+ *   groups = if num_groups > 0: the E experts form num_groups groups of
+ *            E/num_groups consecutive experts; a group scores the fp32 sum
+ *            of its K/group_topk largest fp32 values s + bias (bias 0 when
+ *            absent); only the group_topk best groups (ties: lower group)
+ *            compete.
+ *   select = the K competing experts with the largest key; ties go to the
+ *            lower expert index.  Exact: the map is fully determined.
+ *   p      = s, or with renorm s / (sum of s over the selected experts)
+ *            (sigmoid with K == 1 keeps p = s).
+ *   probs  = scaling_factor * p on the selected experts, exactly 0 elsewhere.
+ *   routing_map  = 1 on the selected experts, 0 elsewhere.
+ *   intermediate = s for every expert (fp32).
+ * expert_bias ([E] fp32, or NULL) affects the selection only, and is only
+ * accepted with the sigmoid (else ROUTER_ERR_UNSUPPORTED).
+ * Checks: T >= 0; 1 <= E <= ROUTER_MAX_EXPERTS (larger E: UNSUPPORTED);
+ * 1 <= K <= E; num_groups >= 0; with num_groups > 0: E % num_groups == 0,
+ * 1 <= group_topk <= num_groups, K % group_topk == 0 and
+ * K / group_topk <= E / num_groups; scaling_factor finite; known dtype and
+ * score_fn; non-NULL arrays when T > 0.
+ */
+router_status router_topk_fwd(const void *logits, int dtype, int64_t T,
+                              int32_t E, int32_t K, int score_fn, int renorm,
+                              int32_t num_groups, int32_t group_topk,
+                              float scaling_factor, const float *expert_bias,
+                              void *probs, uint8_t *routing_map,
+                              float *intermediate, void *hip_stream);
+
+/*
+ * router_topk_bwd -- fused_topk_with_score_function backward.
+ * Passage: the fused-router page, "Backward kernels" (pass 1 reduces
+ * per-token sums of grad * mask * score; pass 2 writes one gradient per
+ * element; inputs are the gradient, the forward's intermediate and its
+ * routing map).
+ *
+ * Given g = grad_probs, s = intermediate and m = routing_map of one token,
+ * with A = sum m s and B = sum g m s and c = scaling_factor:
+ *   softmax, no renorm:    dx = c s (m g - B)
+ *   softmax, renorm:       dx = c m (s / A) (g - B / A)
+ *   sigmoid, no renorm or K == 1: dx = c m g s (1 - s)
+ *   sigmoid, renorm, K > 1: dx = c m s (1 - s) (g - B / A) / A
+ * grad_logits is written in `dtype`.  Checks as router_topk_fwd (T, E, K,
+ * dtype, score_fn, scaling_factor, non-NULL arrays).
+ */
+router_status router_topk_bwd(const void *grad_probs,
+                              const float *intermediate,
+                              const uint8_t *routing_map, int dtype,
+                              int64_t T, int32_t E, int32_t K, int score_fn,
+                              int renorm, float scaling_factor,
+                              void *grad_logits, void *hip_stream);
+
+/*
+ * router_aux_scores -- fused_score_for_moe_aux_loss forward.
+ * Passage: the fused-router page, "Summary" (the aux-loss score operation)
+ * and the benchmark rows "aux_loss fprop".
+ *
+ * Per token: s = softmax(x) or sigmoid(x).  scores = s for softmax; for the
+ * sigmoid scores = s / (sum of s over all E) when renorm, else s.
+ * routing_map = the K largest logits (ties: lower index).  intermediate = s.
+ * scores are written in `dtype`.  Checks as router_topk_fwd (no groups,
+ * no bias).
+ */
+router_status router_aux_scores(const void *logits, int dtype, int64_t T,
+                                int32_t E, int32_t K, int score_fn,
+                                int renorm, void *scores,
+                                uint8_t *routing_map, float *intermediate,
+                                void *hip_stream);
+
+/*
+ * router_aux_scores_bwd -- fused_score_for_moe_aux_loss backward.
+ * Passage: the fused-router page, "Backward kernels" and the benchmark rows
+ * "aux_loss bprop".
+ *
+ * The topk backward with every expert routed and no scaling factor: with
+ * A = sum s and B = sum g s,
+ *   softmax:                dx = s (g - B)
+ *   sigmoid, renorm:        dx = s (1 - s) (g - B / A) / A
+ *   sigmoid, no renorm:     dx = g s (1 - s)
+ */
+router_status router_aux_scores_bwd(const void *grad_scores,
+                                    const float *intermediate, int dtype,
+                                    int64_t T, int32_t E, int score_fn,
+                                    int renorm, void *grad_logits,
+                                    void *hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char *router_status_str(router_status s);
+
+/*
+ * Top-k path threshold.  Passage: the fused-router page, "Simple kernel
+ * path for small topk" and its tunable crossover variable.
+ * K below the threshold selects by K rounds of a lane-group argmax; K at or
+ * above it selects through a pruned candidate sort (an exact bit-wise
+ * search when K exceeds the lanes per token or the pruning leaves too many
+ * candidates).  Every path returns the same map.  The threshold is read
+ * once from the environment variable ROUTER_TOPK_PATH_THRESHOLD (default
+ * 8; a value that is not an integer in [0, 4096] keeps the default) and can
+ * be overridden with router_set_topk_path_threshold, which rejects values
+ * outside [0, 4096] with ROUTER_ERR_INVALID_ARG.
+ */
+int router_get_topk_path_threshold(void);
+router_status router_set_topk_path_threshold(int threshold);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCORE_FUNCTION_TOP_AMD_ROUTER_H */

@@ -1,0 +1,59 @@
+"""Builds librouter.so (the HIP kernels and the C ABI of include/router.h)
+for gfx950 with hipcc, in-tree next to this file.
+
+Each kernel translation unit compiles in its own hipcc process, in
+parallel; objects go to _build/ and are linked into one shared library.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "librouter.so")
+ARCH = os.environ.get("ROUTER_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["router_api.cpp", "router_lpt16.hip", "router_lpt32.hip",
+           "router_lpt64a.hip", "router_lpt64b.hip", "router_lpt64c.hip",
+           "router_scalar.hip"]
+
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         # packed fp32 VALU forms stay off (see the build notes in DESIGN)
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function",
+         "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _compile(src):
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+    return out, msg
+
+
+def build(jobs=None):
+    """Compiles every source and links librouter.so; returns its path."""
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for _, msg in results:
+        if msg.strip():
+            print(msg, file=sys.stderr)
+    objs = [o for o, _ in results]
+    tmp = LIB + ".tmp"
+    subprocess.run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
+                    "-o", tmp], check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

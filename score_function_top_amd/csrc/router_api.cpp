@@ -1,0 +1,364 @@
+// router_api.cpp -- the C ABI of include/router.h: argument checks, choice
+// of kernel configuration and selection path, launch.
+//
+// Host-side hardening follows the "Hardening" list of "[Common] Optimize
+// fused router forward/backward kernels" (NVIDIA TransformerEngine pull
+// request 3012): topk in [1, E], topk divisible by group_topk, and an
+// element count that cannot overflow the index arithmetic (here 64-bit
+// offsets, so the bound is the 64-bit byte count).  The top-k path
+// threshold mirrors that page's crossover variable ("Simple kernel path for
+// small topk"; default 8).
+#include "router.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cerrno>
+#include <cmath>
+#include <cstdlib>
+#include <mutex>
+
+#include "router_params.h"
+
+using namespace rker;
+
+namespace {
+
+// ------------------------------------------------------------ threshold
+
+constexpr int kDefaultThreshold = 8;
+std::atomic<int> g_threshold{-1};
+std::once_flag g_threshold_once;
+
+int threshold()
+{
+    std::call_once(g_threshold_once, [] {
+        int v = kDefaultThreshold;
+        if (const char *e = std::getenv("ROUTER_TOPK_PATH_THRESHOLD")) {
+            char *end = nullptr;
+            errno = 0;
+            long x = std::strtol(e, &end, 10);
+            if (errno == 0 && end != e && *end == '\0' && x >= 0 && x <= ROUTER_MAX_EXPERTS)
+                v = (int)x;
+        }
+        int expect = -1;
+        g_threshold.compare_exchange_strong(expect, v);
+    });
+    return g_threshold.load();
+}
+
+// ------------------------------------------------------------ devices
+
+struct DevInfo {
+    int cus = 0;
+    size_t lds_per_block = 0;
+};
+
+constexpr int kMaxDevices = 64;
+DevInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+// Device attributes, read once per device.
+hipError_t dev_info(DevInfo *out)
+{
+    int d = 0;
+    hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess)
+        return e;
+    if (d < 0 || d >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    hipError_t err = hipSuccess;
+    std::call_once(g_dev_once[d], [&] {
+        int cus = 0, lds = 0;
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d);
+        if (err == hipSuccess)
+            err = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, d);
+        if (err == hipSuccess) {
+            g_dev[d].cus = cus;
+            g_dev[d].lds_per_block = (size_t)lds;
+        }
+    });
+    if (err != hipSuccess)
+        return err;
+    if (g_dev[d].cus <= 0)
+        return hipErrorInvalidDevice;
+    *out = g_dev[d];
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------ checks
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t dsize(int dtype) { return dtype == ROUTER_BF16 ? 2 : 4; }
+
+router_status check_common(int dtype, int64_t T, int32_t E, int score_fn)
+{
+    if (dtype != ROUTER_F32 && dtype != ROUTER_BF16)
+        return ROUTER_ERR_INVALID_ARG;
+    if (score_fn != ROUTER_SOFTMAX && score_fn != ROUTER_SIGMOID)
+        return ROUTER_ERR_INVALID_ARG;
+    if (T < 0 || E < 1)
+        return ROUTER_ERR_INVALID_ARG;
+    if (E > ROUTER_MAX_EXPERTS)
+        return ROUTER_ERR_UNSUPPORTED;
+    // bytes of the largest [T,E] array (fp32 intermediate) must fit int64
+    if (T > INT64_MAX / ((int64_t)E * 4))
+        return ROUTER_ERR_OVERFLOW;
+    return ROUTER_OK;
+}
+
+// ------------------------------------------------------------ configs
+
+struct Cfg {
+    int lpt;
+    int nch;
+    bool vec;
+};
+
+template <size_t N>
+int pick_nch(const int (&list)[N], int need)
+{
+    for (size_t i = 0; i < N; i++)
+        if (list[i] >= need)
+            return list[i];
+    return -1;
+}
+
+int lpt_for_rows(int E) { return E <= 256 ? 16 : (E <= 512 ? 32 : 64); }
+
+// Fills nch for c.lpt / c.vec; false when no built kernel holds E.
+bool fill_nch(Cfg &c, int E)
+{
+    const int need = (E + 4 * c.lpt - 1) / (4 * c.lpt);
+    if (!c.vec)
+        c.nch = pick_nch(kNchScalar, need);
+    else if (c.lpt == 16)
+        c.nch = pick_nch(kNchLpt16, need);
+    else if (c.lpt == 32)
+        c.nch = pick_nch(kNchLpt32, need);
+    else
+        c.nch = pick_nch(kNchLpt64, need);
+    return c.nch > 0;
+}
+
+int widen(int lpt, int need) { return need <= lpt ? lpt : (need <= 32 ? 32 : 64); }
+
+hipError_t launch_fwd(const Cfg &c, int dtype, int score, bool grouped, const FwdParams &p,
+                      const Launch &l)
+{
+    hipError_t err = hipErrorInvalidValue;
+    if (fwd_lpt16(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
+        fwd_lpt32(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
+        fwd_lpt64a(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
+        fwd_lpt64b(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
+        fwd_lpt64c(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
+        fwd_scalar(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err))
+        return err;
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const Cfg &c, int dtype, int score, const BwdParams &p, const Launch &l)
+{
+    hipError_t err = hipErrorInvalidValue;
+    if (bwd_lpt16(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
+        bwd_lpt32(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
+        bwd_lpt64a(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
+        bwd_lpt64b(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
+        bwd_lpt64c(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
+        bwd_scalar(c.lpt, c.nch, c.vec, dtype, score, p, l, &err))
+        return err;
+    return hipErrorInvalidValue;
+}
+
+unsigned grid_for(int64_t T, int lpt)
+{
+    const int64_t tpb = (int64_t)kWaves * (64 / lpt);
+    int64_t blocks = (T + tpb - 1) / tpb;
+    const int64_t cap = (int64_t)1 << 22;  // the kernels stride over the rest
+    return (unsigned)(blocks < cap ? blocks : cap);
+}
+
+// Shared forward path of router_topk_fwd and router_aux_scores.
+router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t K,
+                         int score_fn, int renorm, int32_t G, int32_t Kg, float scale,
+                         const float *bias, void *out, uint8_t *map, float *inter,
+                         void *stream, bool aux)
+{
+    router_status st = check_common(dtype, T, E, score_fn);
+    if (st != ROUTER_OK)
+        return st;
+    if (K < 1 || K > E || G < 0)
+        return ROUTER_ERR_INVALID_ARG;
+    if (G > 0 && (E % G != 0 || Kg < 1 || Kg > G || K % Kg != 0 || K / Kg > E / G))
+        return ROUTER_ERR_INVALID_ARG;
+    if (!std::isfinite(scale))
+        return ROUTER_ERR_INVALID_ARG;
+    if (bias && score_fn != ROUTER_SIGMOID)
+        return ROUTER_ERR_UNSUPPORTED;
+    if (G > 64)
+        return ROUTER_ERR_UNSUPPORTED;
+    if (T == 0)
+        return ROUTER_OK;
+    if (!x || !out || !map || !inter)
+        return ROUTER_ERR_INVALID_ARG;
+    const size_t ds = dsize(dtype);
+    if (!aligned(x, ds) || !aligned(out, ds) || !aligned(inter, 4) || (bias && !aligned(bias, 4)))
+        return ROUTER_ERR_INVALID_ARG;
+
+    const bool vec = E % 4 == 0 && aligned(x, 16) && aligned(out, 16) && aligned(inter, 16) &&
+                     aligned(map, 16) && (!bias || aligned(bias, 16));
+    const int thr = threshold();
+    int sel = K < thr ? SEL_ARGMAX : SEL_PRUNE;
+    Cfg c{vec ? lpt_for_rows(E) : 64, 0, vec};
+    if (sel == SEL_PRUNE)
+        c.lpt = widen(c.lpt, K);
+    if (G > 0)
+        c.lpt = widen(c.lpt, G);
+    if (!fill_nch(c, E))
+        return ROUTER_ERR_UNSUPPORTED;
+    if (sel == SEL_PRUNE && K > c.lpt)
+        sel = SEL_BITS;
+
+    DevInfo dev;
+    if (dev_info(&dev) != hipSuccess)
+        return ROUTER_ERR_HIP;
+    const int tpb = kWaves * (64 / c.lpt);
+    size_t smem = (size_t)tpb * cand_slots(c.lpt) * sizeof(uint64_t);
+    if (G > 0)
+        smem += (size_t)tpb * group_scratch_floats(E, G, c.lpt) * sizeof(float);
+    if (smem > dev.lds_per_block)
+        return ROUTER_ERR_UNSUPPORTED;
+
+    FwdParams p{};
+    p.x = x;
+    p.out = out;
+    p.map = map;
+    p.inter = inter;
+    p.bias = bias;
+    p.T = T;
+    p.E = E;
+    p.K = K;
+    p.sel = sel;
+    p.renorm = renorm ? 1 : 0;
+    p.aux = aux ? 1 : 0;
+    p.G = G;
+    p.Kg = G > 0 ? Kg : 0;
+    p.q = G > 0 ? K / Kg : 0;
+    p.P = G > 0 ? E / G : 0;
+    p.scale = scale;
+    const Launch l{grid_for(T, c.lpt), smem, (hipStream_t)stream};
+    return launch_fwd(c, dtype, score_fn, G > 0, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+router_status bwd_common(const void *g, const float *s, const uint8_t *m, int dtype, int64_t T,
+                         int32_t E, int32_t K, int score_fn, int renorm, float scale, void *dx,
+                         void *stream)
+{
+    router_status st = check_common(dtype, T, E, score_fn);
+    if (st != ROUTER_OK)
+        return st;
+    if (K < 1 || K > E)
+        return ROUTER_ERR_INVALID_ARG;
+    if (!std::isfinite(scale))
+        return ROUTER_ERR_INVALID_ARG;
+    if (T == 0)
+        return ROUTER_OK;
+    const bool aux = m == nullptr;
+    if (!g || !s || !dx)
+        return ROUTER_ERR_INVALID_ARG;
+    const size_t ds = dsize(dtype);
+    if (!aligned(g, ds) || !aligned(dx, ds) || !aligned(s, 4))
+        return ROUTER_ERR_INVALID_ARG;
+    const bool vec = E % 4 == 0 && aligned(g, 16) && aligned(dx, 16) && aligned(s, 16) &&
+                     (aux || aligned(m, 16));
+    Cfg c{vec ? lpt_for_rows(E) : 64, 0, vec};
+    if (!fill_nch(c, E))
+        return ROUTER_ERR_UNSUPPORTED;
+    DevInfo dev;
+    if (dev_info(&dev) != hipSuccess)
+        return ROUTER_ERR_HIP;
+    BwdParams p{};
+    p.g = g;
+    p.s = s;
+    p.m = m;
+    p.dx = dx;
+    p.T = T;
+    p.E = E;
+    p.K = K;
+    p.renorm = renorm ? 1 : 0;
+    p.scale = scale;
+    const Launch l{grid_for(T, c.lpt), 0, (hipStream_t)stream};
+    return launch_bwd(c, dtype, score_fn, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+router_status router_topk_fwd(const void *logits, int dtype, int64_t T, int32_t E, int32_t K,
+                              int score_fn, int renorm, int32_t num_groups, int32_t group_topk,
+                              float scaling_factor, const float *expert_bias, void *probs,
+                              uint8_t *routing_map, float *intermediate, void *hip_stream)
+{
+    return fwd_common(logits, dtype, T, E, K, score_fn, renorm, num_groups, group_topk,
+                      scaling_factor, expert_bias, probs, routing_map, intermediate, hip_stream,
+                      false);
+}
+
+router_status router_topk_bwd(const void *grad_probs, const float *intermediate,
+                              const uint8_t *routing_map, int dtype, int64_t T, int32_t E,
+                              int32_t K, int score_fn, int renorm, float scaling_factor,
+                              void *grad_logits, void *hip_stream)
+{
+    if (T > 0 && !routing_map)
+        return ROUTER_ERR_INVALID_ARG;
+    return bwd_common(grad_probs, intermediate, routing_map, dtype, T, E, K, score_fn, renorm,
+                      scaling_factor, grad_logits, hip_stream);
+}
+
+router_status router_aux_scores(const void *logits, int dtype, int64_t T, int32_t E, int32_t K,
+                                int score_fn, int renorm, void *scores, uint8_t *routing_map,
+                                float *intermediate, void *hip_stream)
+{
+    return fwd_common(logits, dtype, T, E, K, score_fn, renorm, 0, 0, 1.0f, nullptr, scores,
+                      routing_map, intermediate, hip_stream, true);
+}
+
+router_status router_aux_scores_bwd(const void *grad_scores, const float *intermediate,
+                                    int dtype, int64_t T, int32_t E, int score_fn, int renorm,
+                                    void *grad_logits, void *hip_stream)
+{
+    return bwd_common(grad_scores, intermediate, nullptr, dtype, T, E, E > 0 ? E : 1, score_fn,
+                      renorm, 1.0f, grad_logits, hip_stream);
+}
+
+const char *router_status_str(router_status s)
+{
+    switch (s) {
+    case ROUTER_OK:
+        return "ROUTER_OK";
+    case ROUTER_ERR_INVALID_ARG:
+        return "ROUTER_ERR_INVALID_ARG: argument outside the operation's domain";
+    case ROUTER_ERR_OVERFLOW:
+        return "ROUTER_ERR_OVERFLOW: T*E*element size overflows 64 bits";
+    case ROUTER_ERR_UNSUPPORTED:
+        return "ROUTER_ERR_UNSUPPORTED: valid arguments this library does not implement";
+    case ROUTER_ERR_HIP:
+        return "ROUTER_ERR_HIP: a HIP call or kernel launch failed";
+    }
+    return "unknown router_status";
+}
+
+int router_get_topk_path_threshold(void) { return threshold(); }
+
+router_status router_set_topk_path_threshold(int t)
+{
+    if (t < 0 || t > ROUTER_MAX_EXPERTS)
+        return ROUTER_ERR_INVALID_ARG;
+    threshold();  // the environment is read first, then overridden
+    g_threshold.store(t);
+    return ROUTER_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,722 @@
+// router_kernels.h -- forward and backward kernels of the fused MoE router
+// for gfx950.
+//
+// Operations: fused_topk_with_score_function and fused_score_for_moe_aux_loss
+// ("[Common] Optimize fused router forward/backward kernels", NVIDIA
+// TransformerEngine pull request 3012, "Summary", "Forward kernels",
+// "Backward kernels").  The per-token maths is stated in include/router.h.
+//
+// Work split: one token per lane group of LPT lanes (16, 32 or 64), 64/LPT
+// tokens per wave, 4 waves per 256-thread block, grid-stride over tokens.
+// Lane l of a group holds NCH chunks of 4 consecutive elements: element
+// j = c*4*LPT + 4*l + u for chunk c and component u, so every chunk load
+// or store of a group is one contiguous segment.  The whole row lives in
+// VGPRs; LDS holds only a 2*LPT candidate list per token (and, for grouped
+// routing, the row's group values).
+//
+// Selection of the K largest keys (ties to the lower index) is exact and
+// reduces to one 64-bit threshold: with pack(j) = key_j << 32 | ~j (unique
+// per element), expert j is selected iff pack(j) >= T64, where T64 is the
+// K-th largest pack value.  Ways to find it:
+//   argmax  K rounds of a group-wide max whose winner is marked (small K);
+//   prune   tau = K-th largest lane maximum bounds the K-th largest key from
+//           below (K lanes hold a key >= tau), so only keys >= tau compete;
+//           they are compacted into LDS (at most 2*LPT of them) and
+//           bitonic-sorted across the lanes (K <= LPT);
+//   bits    exact bit-by-bit search of the K-th key value, then of the index
+//           among equal keys (any K; taken when pruning leaves more than
+//           2*LPT candidates, or when K > LPT).
+//
+// Code shape: no branch depends on a single element.  Padding is encoded in
+// the data (key 0, score 0); stores of masked chunks get a byte offset past
+// the buffer's range, which the hardware drops.
+#pragma once
+
+#include "router_device.h"
+#include "router_params.h"
+
+namespace rker {
+
+using namespace rdev;
+
+// ------------------------------------------------------------ row I/O
+//
+// Global traffic goes through raw buffer resources: one descriptor per wave
+// covering the rows of the wave's tokens (base and byte count in SGPRs) and
+// a 32-bit per-lane byte offset.  Loads past the range read 0 and stores
+// past it are dropped, which retires the tail tokens of the last wave and
+// masked chunks without branches.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr uint32_t kOOB = 0x80000000u;  // byte offset outside every buffer
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // 0x00020000: raw 32-bit data format word for the gfx9 family
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)bytes, 0x00020000);
+}
+
+template <typename TIn> struct io;
+
+template <> struct io<float> {
+    static constexpr uint32_t kSize = 4;
+    __device__ static void load4(rsrc_t r, uint32_t off, uint32_t soff, float (&v)[4])
+    {
+        auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0);
+        v[0] = as_f(t[0]); v[1] = as_f(t[1]); v[2] = as_f(t[2]); v[3] = as_f(t[3]);
+    }
+    __device__ static float load1(rsrc_t r, uint32_t off)
+    {
+        return as_f(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+    __device__ static void store4(rsrc_t r, uint32_t off, const float (&v)[4])
+    {
+        __attribute__((ext_vector_type(4))) uint32_t t;
+        t[0] = as_u(v[0]); t[1] = as_u(v[1]); t[2] = as_u(v[2]); t[3] = as_u(v[3]);
+        __builtin_amdgcn_raw_buffer_store_b128(t, r, (int)off, 0, 0);
+    }
+    __device__ static void store1(rsrc_t r, uint32_t off, float v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(as_u(v), r, (int)off, 0, 0);
+    }
+};
+
+template <> struct io<uint16_t> {
+    static constexpr uint32_t kSize = 2;
+    __device__ static void load4(rsrc_t r, uint32_t off, uint32_t soff, float (&v)[4])
+    {
+        auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0);
+        v[0] = as_f(t[0] << 16); v[1] = as_f(t[0] & 0xFFFF0000u);
+        v[2] = as_f(t[1] << 16); v[3] = as_f(t[1] & 0xFFFF0000u);
+    }
+    __device__ static float load1(rsrc_t r, uint32_t off)
+    {
+        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+    }
+    __device__ static void store4(rsrc_t r, uint32_t off, const float (&v)[4])
+    {
+        __attribute__((ext_vector_type(2))) uint32_t t;
+        t[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        t[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(t, r, (int)off, 0, 0);
+    }
+    __device__ static void store1(rsrc_t r, uint32_t off, float v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)off, 0, 0);
+    }
+};
+
+// Element index of chunk c, component u relative to this lane (the lane's
+// part, j_lane = 4*lane, is added by the caller).
+template <int LPT>
+__device__ __forceinline__ constexpr int jrel(int c, int u) { return c * 4 * LPT + u; }
+
+// Loads chunk c of the group's row (element offset goff in the wave's
+// buffer).  With VEC one 4-element vector access (lane offset in a VGPR,
+// chunk offset in the scalar offset), else four element accesses.
+// Elements at or past Ev read as `pad`.  A masked access gets the VGPR
+// offset kOOB, which is out of range whether or not the hardware adds the
+// scalar offset to its range check, so it never touches memory.
+template <int LPT, typename T, bool VEC>
+__device__ __forceinline__ void load_chunk(rsrc_t r, uint32_t goff, int c, int j_lane,
+                                           int Ev, float pad, float (&v)[4])
+{
+    const int j0 = jrel<LPT>(c, 0) + j_lane;
+    if constexpr (VEC) {
+        const bool ok = j0 < Ev;
+        io<T>::load4(r, ok ? (goff + (uint32_t)j_lane) * io<T>::kSize : kOOB,
+                     (uint32_t)jrel<LPT>(c, 0) * io<T>::kSize, v);
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            v[u] = ok ? v[u] : pad;
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const bool ok = j0 + u < Ev;
+            const float t = io<T>::load1(r, ok ? (goff + (uint32_t)(j0 + u)) * io<T>::kSize : kOOB);
+            v[u] = ok ? t : pad;
+        }
+    }
+}
+
+template <int LPT, typename T, bool VEC>
+__device__ __forceinline__ void store_chunk(rsrc_t r, uint32_t goff, int c, int j_lane,
+                                            int E, const float (&v)[4])
+{
+    const int j0 = jrel<LPT>(c, 0) + j_lane;
+    if constexpr (VEC) {
+        io<T>::store4(r, j0 < E ? (goff + (uint32_t)j0) * io<T>::kSize : kOOB, v);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            io<T>::store1(r, j0 + u < E ? (goff + (uint32_t)(j0 + u)) * io<T>::kSize : kOOB,
+                          v[u]);
+    }
+}
+
+// Map bytes of chunk c, little-endian in one u32 (0 past Ev).
+template <int LPT, bool VEC>
+__device__ __forceinline__ uint32_t load_map_chunk(rsrc_t r, uint32_t goff, int c,
+                                                   int j_lane, int Ev)
+{
+    const int j0 = jrel<LPT>(c, 0) + j_lane;
+    if constexpr (VEC) {
+        const bool ok = j0 < Ev;
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+            r, (int)(ok ? goff + (uint32_t)j_lane : kOOB), jrel<LPT>(c, 0), 0);
+        return ok ? w : 0u;
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(
+                r, (int)(j0 + u < Ev ? goff + (uint32_t)(j0 + u) : kOOB), 0, 0);
+            w |= b << (8 * u);
+        }
+        return w;
+    }
+}
+
+template <int LPT, bool VEC>
+__device__ __forceinline__ void store_map_chunk(rsrc_t r, uint32_t goff, int c, int j_lane,
+                                                int E, uint32_t w)
+{
+    const int j0 = jrel<LPT>(c, 0) + j_lane;
+    if constexpr (VEC) {
+        __builtin_amdgcn_raw_buffer_store_b32(w, r, (int)(j0 < E ? goff + (uint32_t)j0 : kOOB),
+                                              0, 0);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            __builtin_amdgcn_raw_buffer_store_b8(
+                (uint8_t)(w >> (8 * u)), r,
+                (int)(j0 + u < E ? goff + (uint32_t)(j0 + u) : kOOB), 0, 0);
+    }
+}
+
+// Pairwise (tree) sum of N values held in registers.
+template <int N, int O = 0>
+__device__ __forceinline__ float tree_sum(const float *v)
+{
+    if constexpr (N == 1) {
+        return v[O];
+    } else {
+        constexpr int H = N / 2;
+        return tree_sum<H, O>(v) + tree_sum<N - H, O + H>(v);
+    }
+}
+
+__device__ __forceinline__ uint64_t pack_key(uint32_t key, uint32_t j)
+{
+    return key ? (((uint64_t)key << 32) | (uint32_t)~j) : 0ull;
+}
+
+// Key of a logit: 0 for padding (-inf), else the order-preserving key of
+// x + 0.0 (so that -0.0 and +0.0, equal logits, tie).
+__device__ __forceinline__ uint32_t logit_key(float x)
+{
+    return x == -INFINITY ? 0u : ord_key(x + 0.0f);
+}
+
+// ------------------------------------------------------------ selection
+
+// Marks a selected expert during argmax rounds: below every real key
+// (>= 0x00800000) and above the "no candidate" 0.
+constexpr uint32_t kTaken = 1u;
+
+// argmax: K rounds; each round the group's largest pack value wins and its
+// key becomes kTaken.  Afterwards the selected experts are the kTaken keys.
+template <int LPT, int NCH>
+__device__ __forceinline__ void select_argmax(uint32_t (&key)[NCH][4], int K, int j_lane)
+{
+    for (int r = 0; r < K; r++) {
+        // lane-local best: first (lowest j) element with the largest key
+        uint32_t bk = key[0][0];
+        uint32_t bj = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                if (c == 0 && u == 0)
+                    continue;
+                const bool gt = key[c][u] > bk;
+                bk = gt ? key[c][u] : bk;
+                bj = gt ? (uint32_t)jrel<LPT>(c, u) : bj;
+            }
+        const uint64_t best =
+            group_max_u64<LPT>(pack_key(bk > kTaken ? bk : 0u, bj + (uint32_t)j_lane));
+        // winner's j relative to this lane; no match when there is no winner
+        const uint32_t jw = best ? ~(uint32_t)best - (uint32_t)j_lane : 0xFFFFFFFFu;
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                key[c][u] = jw == (uint32_t)jrel<LPT>(c, u) ? kTaken : key[c][u];
+    }
+}
+
+// bits: exact search, any K.  Finds the K-th largest key value v, then
+// among keys equal to v the index of the (K - #{key > v})-th lowest.
+template <int LPT, int NCH>
+__device__ __forceinline__ uint64_t select_bits(const uint32_t (&key)[NCH][4],
+                                                int K, int j_lane)
+{
+    uint32_t pref = 0;
+    for (int b = 31; b >= 0; b--) {
+        const uint32_t cand = pref | (1u << b);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                cnt += key[c][u] >= cand;
+        pref = group_sum_u32<LPT>(cnt) >= (uint32_t)K ? cand : pref;
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            gt += key[c][u] > pref;
+            eq += key[c][u] == pref;
+        }
+    gt = group_sum_u32<LPT>(gt);
+    eq = group_sum_u32<LPT>(eq);
+    const uint32_t need = (uint32_t)K - gt;
+    uint32_t J = 0xFFFFFFFFu;  // every key equal to pref is selected
+    if (wave_any(eq != need)) {
+        // lowest J with #{key == pref, j <= J} >= need
+        uint32_t lo = 0;
+        for (int b = 31 - __builtin_clz(NCH * 4 * LPT); b >= 0; b--) {
+            const int test = (int)(lo + (1u << b) - 1u) - j_lane;  // lane-relative
+            uint32_t f = 0;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    f += (key[c][u] == pref) & (jrel<LPT>(c, u) <= test);
+            lo = group_sum_u32<LPT>(f) < need ? lo + (1u << b) : lo;
+        }
+        J = eq != need ? lo : J;
+    }
+    return ((uint64_t)pref << 32) | (uint32_t)~J;
+}
+
+// prune: candidates >= tau (the K-th largest lane maximum) compacted into
+// this group's LDS list, sorted, K-th taken.  The list has 2*LPT slots plus
+// one dummy slot per lane that absorbs the writes of non-candidates.  Falls
+// back to select_bits for the whole wave when a group has more than 2*LPT
+// candidates.  Requires K <= LPT.
+template <int LPT, int NCH>
+__device__ __forceinline__ uint64_t select_prune(const uint32_t (&key)[NCH][4],
+                                                 int K, int lane, int j_lane,
+                                                 uint64_t *cand)
+{
+    uint32_t lm = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            lm = key[c][u] > lm ? key[c][u] : lm;
+    uint32_t tau = group_bcast<LPT>(sort_desc32<LPT>(lm), K - 1);
+    tau = tau ? tau : 1u;  // padding and excluded experts never compete
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            cnt += key[c][u] >= tau;
+    const uint32_t incl = group_incl_scan<LPT>(cnt);
+    const uint32_t total = group_bcast<LPT>(incl, LPT - 1);
+    if (wave_any(total > 2u * LPT))
+        return select_bits<LPT, NCH>(key, K, j_lane);
+    uint32_t pos = incl - cnt;
+    const uint32_t dummy = 2u * LPT + (uint32_t)lane;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const bool in = key[c][u] >= tau;
+            cand[in ? pos : dummy] = pack_key(key[c][u], (uint32_t)(jrel<LPT>(c, u) + j_lane));
+            pos += in;
+        }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint64_t v0 = cand[lane];
+    v0 = (uint32_t)lane < total ? v0 : 0ull;
+    if (wave_any(total > (uint32_t)LPT)) {
+        uint64_t v1 = cand[lane + LPT];
+        v1 = (uint32_t)(lane + LPT) < total ? v1 : 0ull;
+        sort_desc64x2<LPT>(v0, v1);
+    } else {
+        v0 = sort_desc64<LPT>(v0);
+    }
+    const uint64_t t64 = group_bcast64<LPT>(v0, K - 1);  // K <= LPT: in the first half
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    return t64;
+}
+
+// Group-limited routing.  Group g = experts [g*P, (g+1)*P); its score is
+// the fp32 sum of its q largest values s + b, largest first; the Kg best
+// groups stay (ties keep the lower group) and the keys of every other
+// expert are cleared.  The caller first stores each element's value with
+// group_value_store into gscr (group_scratch_floats(E, G, LPT) floats of
+// LDS for this token group: one padding word after each group so the
+// per-group scans touch distinct banks, and a dummy word per lane for
+// padding elements).  Requires G <= LPT.
+
+__device__ __forceinline__ int group_of(int j, float invP)
+{
+    return (int)(((float)j + 0.5f) * invP);  // exact for E <= 2^20
+}
+
+__device__ __forceinline__ void group_value_store(float *gscr, int j, bool real, float v,
+                                                  const FwdParams &p, float invP, int lane)
+{
+    gscr[real ? j + group_of(j, invP) : p.E + p.G + lane] = v;
+}
+
+template <int LPT, int NCH>
+__device__ __forceinline__ void group_limit(uint32_t (&key)[NCH][4], const FwdParams &p,
+                                            int lane, int j_lane, bool tok, float invP,
+                                            const float *gscr)
+{
+    const int G = p.G, P = p.P;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float h = -INFINITY;
+    if (lane < G && tok) {
+        const float *gv = gscr + lane * (P + 1);
+        if (p.q == 1) {
+            float m1 = -INFINITY;
+            for (int i = 0; i < P; i++)
+                m1 = fmaxf(m1, gv[i]);
+            h = m1;
+        } else if (p.q == 2) {
+            float m1 = -INFINITY, m2 = -INFINITY;
+            for (int i = 0; i < P; i++) {
+                const float v = gv[i];
+                m2 = fmaxf(m2, fminf(m1, v));
+                m1 = fmaxf(m1, v);
+            }
+            h = m1 + m2;
+        } else {
+            // q rounds, each taking the next largest (value, lower index)
+            float acc = 0.0f, pv = INFINITY;
+            int pi = -1;
+            for (int r = 0; r < p.q; r++) {
+                float bv = -INFINITY;
+                int bi = P;
+                for (int i = 0; i < P; i++) {
+                    const float v = gv[i];
+                    const bool below = v < pv || (v == pv && i > pi);
+                    const bool better = v > bv || (v == bv && i < bi);
+                    bv = (below && better) ? v : bv;
+                    bi = (below && better) ? i : bi;
+                }
+                acc = acc + bv;
+                pv = bv;
+                pi = bi;
+            }
+            h = acc;
+        }
+    }
+    // rank of group `lane` among the G scores (ties: lower group)
+    uint32_t rank = 0;
+    for (int g2 = 0; g2 < G; g2++) {
+        const float o = as_f(group_bcast<LPT>(as_u(h), g2));
+        rank += (o > h) || (o == h && g2 < lane);
+    }
+    const bool kept = lane < G && rank < (uint32_t)p.Kg;
+    const uint64_t gmask = __builtin_amdgcn_ballot_w64(kept) >> (lane_id() & ~(LPT - 1));
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int g = group_of(jrel<LPT>(c, u) + j_lane, invP);
+            const bool in = g < G && ((gmask >> (g & 63)) & 1ull);
+            key[c][u] = in ? key[c][u] : 0u;
+        }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ------------------------------------------------------------ forward
+
+// SEL_ARGMAX kernels run the argmax rounds; SEL_PRUNE kernels run the
+// pruned sort, or the bit search when p.sel == SEL_BITS.  GROUPED kernels
+// add group-limited routing (p.G > 0).
+template <int LPT, int NCH, typename TIn, int SCORE, int SEL, bool GROUPED, bool VEC>
+__global__ void __launch_bounds__(kBlock)
+fwd_kernel(FwdParams p)
+{
+    constexpr int GPW = 64 / LPT;            // token groups per wave
+    constexpr int TPB = kWaves * GPW;        // tokens per block
+    constexpr int VPL = NCH * 4;
+    extern __shared__ uint64_t smem[];
+
+    const int lane64 = lane_id();
+    const int lane = lane64 & (LPT - 1);
+    const int j_lane = 4 * lane;
+    const int grp = lane64 / LPT;                          // group in wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gslot = wave * GPW + grp;                    // group in block
+    uint64_t *cand = smem + gslot * cand_slots(LPT);
+    const int E = p.E;
+    const uint32_t goff = (uint32_t)(grp * E);             // group row in the wave buffer
+    const bool has_bias = p.bias != nullptr;
+
+    for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
+         tb += (int64_t)gridDim.x * TPB) {
+        const int64_t t0 = tb + wave * GPW;                // first token of the wave
+        const int64_t left = p.T - t0;
+        const int nval = left <= 0 ? 0 : (left >= GPW ? GPW : (int)left);
+        const bool tok = grp < nval;
+        const int Ev = tok ? E : 0;
+        const int64_t off0 = nval ? t0 * (int64_t)E : 0;
+        const uint32_t nel = (uint32_t)(nval * E);
+        const rsrc_t rx = make_rsrc(static_cast<const TIn *>(p.x) + off0, nel * io<TIn>::kSize);
+
+        float x[NCH][4];
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+            load_chunk<LPT, TIn, VEC>(rx, goff, c, j_lane, Ev, -INFINITY, x[c]);
+        __builtin_amdgcn_sched_barrier(0);  // every load in flight before any math
+
+        // ---- score function; logit keys (0 on padding)
+        uint32_t key[NCH][4];
+        float s[NCH][4];
+        float mx = 0.0f;
+        if constexpr (SCORE == SCORE_SOFTMAX) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    m = fmaxf(m, x[c][u]);
+            mx = group_max<LPT>(m);
+            mx = tok ? mx : 0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                key[c][u] = logit_key(x[c][u]);
+                if constexpr (SCORE == SCORE_SOFTMAX)
+                    s[c][u] = expf(x[c][u] - mx);              // padding: exp(-inf) = 0
+                else
+                    s[c][u] = 1.0f / (1.0f + expf(-x[c][u]));  // padding: 0
+            }
+        if constexpr (SCORE == SCORE_SOFTMAX) {
+            const float z = group_sum<LPT>(tree_sum<VPL>(&s[0][0]));
+            const float rz = tok ? 1.0f / z : 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    s[c][u] *= rz;
+        }
+
+        // ---- expert bias (selection only) and group values s + b
+        [[maybe_unused]] float *gscr = nullptr;
+        [[maybe_unused]] float invP = 0.0f;
+        if constexpr (GROUPED) {
+            gscr = reinterpret_cast<float *>(smem + TPB * cand_slots(LPT)) +
+                   gslot * group_scratch_floats(E, p.G, LPT);
+            invP = 1.0f / (float)p.P;
+        }
+        if (has_bias || GROUPED) {
+            const rsrc_t rb = make_rsrc(p.bias, has_bias ? (uint32_t)E * 4u : 0u);
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                float b[4];
+                load_chunk<LPT, float, VEC>(rb, 0u, c, j_lane, Ev, 0.0f, b);
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const float r = s[c][u] + b[u];
+                    const bool real = key[c][u] != 0u;
+                    if constexpr (GROUPED)
+                        group_value_store(gscr, jrel<LPT>(c, u) + j_lane, real, r, p, invP, lane);
+                    if (has_bias)
+                        key[c][u] = real ? ord_key(r + 0.0f) : 0u;
+                }
+            }
+        }
+        if constexpr (GROUPED)
+            group_limit<LPT, NCH>(key, p, lane, j_lane, tok, invP, gscr);
+
+        // ---- top-K; the selection lives in the map words (one byte per
+        // element, chunk-packed), which the store needs anyway
+        uint32_t mw[NCH];
+        if constexpr (SEL == SEL_ARGMAX) {
+            select_argmax<LPT, NCH>(key, p.K, j_lane);
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    w |= (uint32_t)(key[c][u] == kTaken) << (8 * u);
+                mw[c] = w;
+            }
+        } else {
+            const uint64_t t64 = p.sel == SEL_BITS
+                                     ? select_bits<LPT, NCH>(key, p.K, j_lane)
+                                     : select_prune<LPT, NCH>(key, p.K, lane, j_lane, cand);
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const bool in = key[c][u] != 0u &&
+                                    pack_key(key[c][u], (uint32_t)(jrel<LPT>(c, u) + j_lane)) >= t64;
+                    w |= (uint32_t)in << (8 * u);
+                }
+                mw[c] = w;
+            }
+        }
+
+        // ---- weights: out = keep ? s * mult : 0, keep = aux or selected
+        const bool all = p.aux != 0;
+        const uint32_t keep_all = all ? 0x01010101u : 0u;
+        const bool norm = all ? (SCORE == SCORE_SIGMOID && p.renorm)
+                              : (p.renorm && (SCORE == SCORE_SOFTMAX || p.K > 1));
+        float mult = all ? 1.0f : p.scale;
+        if (norm) {
+            float part[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                const uint32_t kw = mw[c] | keep_all;
+                float a4[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    a4[u] = ((kw >> (8 * u)) & 0xFFu) ? s[c][u] : 0.0f;
+                part[c] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+            }
+            const float a = group_sum<LPT>(tree_sum<NCH>(part));
+            mult = tok ? mult / a : 0.0f;
+        }
+
+        // ---- stores (tokens past T fall outside the buffers and are dropped)
+        const rsrc_t ro = make_rsrc(static_cast<TIn *>(p.out) + off0, nel * io<TIn>::kSize);
+        const rsrc_t ri = make_rsrc(p.inter + off0, nel * 4u);
+        const rsrc_t rm = make_rsrc(p.map + off0, nel);
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            const uint32_t kw = mw[c] | keep_all;
+            float o[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                o[u] = ((kw >> (8 * u)) & 0xFFu) ? s[c][u] * mult : 0.0f;
+            store_chunk<LPT, float, VEC>(ri, goff, c, j_lane, E, s[c]);
+            store_chunk<LPT, TIn, VEC>(ro, goff, c, j_lane, E, o);
+            store_map_chunk<LPT, VEC>(rm, goff, c, j_lane, E, mw[c]);
+        }
+    }
+}
+
+// ------------------------------------------------------------ backward
+//
+// Every mode is dx = w * (gm - beta) with per-token uniforms:
+//   w    = base * alpha * (mask_w ? m : 1),  base = s (softmax) or s(1-s)
+//   gm   = mask_g ? m g : g
+//   softmax, no renorm:   alpha = c,    beta = B,   mask_g        (aux: c = 1)
+//   softmax, renorm:      alpha = c/A,  beta = B/A, mask_w
+//   sigmoid, renorm, K>1: alpha = c/A,  beta = B/A, mask_w        (aux: c = 1, m = 1)
+//   sigmoid otherwise:    alpha = c,    beta = 0,   mask_w
+// with A = sum m s and B = sum g m s over the token.
+
+template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
+__global__ void __launch_bounds__(kBlock)
+bwd_kernel(BwdParams p)
+{
+    constexpr int GPW = 64 / LPT;
+    constexpr int TPB = kWaves * GPW;
+
+    const int lane64 = lane_id();
+    const int lane = lane64 & (LPT - 1);
+    const int j_lane = 4 * lane;
+    const int grp = lane64 / LPT;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int E = p.E;
+    const uint32_t goff = (uint32_t)(grp * E);
+    const bool aux = p.m == nullptr;
+    const bool renorm_mode = p.renorm && (SCORE == SCORE_SOFTMAX ? !aux : (aux || p.K > 1));
+    const bool need_b = SCORE == SCORE_SOFTMAX || renorm_mode;
+    const float c0 = aux ? 1.0f : p.scale;
+    const float mask_w = (SCORE == SCORE_SOFTMAX && !renorm_mode) ? 0.0f : 1.0f;
+    const float mask_g = 1.0f - mask_w;
+
+    for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
+         tb += (int64_t)gridDim.x * TPB) {
+        const int64_t t0 = tb + wave * GPW;
+        const int64_t left = p.T - t0;
+        const int nval = left <= 0 ? 0 : (left >= GPW ? GPW : (int)left);
+        const int Ev = grp < nval ? E : 0;
+        const int64_t off0 = nval ? t0 * (int64_t)E : 0;
+        const uint32_t nel = (uint32_t)(nval * E);
+        const rsrc_t rg = make_rsrc(static_cast<const TIn *>(p.g) + off0, nel * io<TIn>::kSize);
+        const rsrc_t rs = make_rsrc(p.s + off0, nel * 4u);
+        const rsrc_t rm = make_rsrc(aux ? nullptr : p.m + off0, aux ? 0u : nel);
+
+        float g[NCH][4], s[NCH][4];
+        uint32_t mw[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            load_chunk<LPT, TIn, VEC>(rg, goff, c, j_lane, Ev, 0.0f, g[c]);
+            load_chunk<LPT, float, VEC>(rs, goff, c, j_lane, Ev, 0.0f, s[c]);
+            mw[c] = load_map_chunk<LPT, VEC>(rm, goff, c, j_lane, Ev);  // aux: 0
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load in flight before any math
+        // aux: every expert routed (padding has s = g = 0 and adds nothing)
+        if (aux) {
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+                mw[c] = 0x01010101u;
+        }
+        float A = 1.0f, B = 0.0f;
+        if (renorm_mode || need_b) {
+            float pa[NCH], pb[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                float a4[4], b4[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    a4[u] = ((mw[c] >> (8 * u)) & 0xFFu) ? s[c][u] : 0.0f;
+                    b4[u] = g[c][u] * a4[u];
+                }
+                pa[c] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+                pb[c] = (b4[0] + b4[1]) + (b4[2] + b4[3]);
+            }
+            if (renorm_mode)
+                A = group_sum<LPT>(tree_sum<NCH>(pa));
+            if (need_b)
+                B = group_sum<LPT>(tree_sum<NCH>(pb));
+        }
+        float alpha = c0, beta = SCORE == SCORE_SOFTMAX ? B : 0.0f;
+        if (renorm_mode) {
+            const float rA = Ev ? 1.0f / A : 0.0f;
+            alpha = c0 * rA;
+            beta = B * rA;
+        }
+        const rsrc_t rd = make_rsrc(static_cast<TIn *>(p.dx) + off0, nel * io<TIn>::kSize);
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            float d[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float sv = s[c][u];
+                const float m = ((mw[c] >> (8 * u)) & 0xFFu) ? 1.0f : 0.0f;
+                const float base = SCORE == SCORE_SOFTMAX ? sv : sv * (1.0f - sv);
+                const float wm = fmaf(mask_w, m - 1.0f, 1.0f);   // mask_w ? m : 1
+                const float gm = g[c][u] * fmaf(mask_g, m - 1.0f, 1.0f);
+                d[u] = (base * alpha * wm) * (gm - beta);
+            }
+            store_chunk<LPT, TIn, VEC>(rd, goff, c, j_lane, E, d);
+        }
+    }
+}
+
+}  // namespace rker

@@ -1,0 +1,105 @@
+// router_launch.h -- host-side launch tables of the router kernels.
+// Internal to the library.
+//
+// Vector kernels (16-byte loads and stores; E % 4 == 0, aligned arrays) are
+// built for lane-group widths LPT = 16, 32, 64 and a list of chunk counts
+// NCH each; a row of E elements takes the smallest built NCH with
+// NCH*4*LPT >= E.  Element-wise kernels (any E, element-aligned arrays) are
+// built for LPT = 64 and NCH in {1, 2, 4, 8, 16}.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "router_kernels.h"
+
+namespace rker {
+
+template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
+hipError_t fwd_one(const FwdParams &p, bool grouped, const Launch &l)
+{
+    dim3 g(l.grid), b(kBlock);
+    if (p.sel == SEL_ARGMAX) {
+        if (grouped)
+            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_ARGMAX, true, VEC>), g, b,
+                               l.smem, l.stream, p);
+        else
+            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_ARGMAX, false, VEC>), g, b,
+                               l.smem, l.stream, p);
+    } else {
+        if (grouped)
+            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_PRUNE, true, VEC>), g, b,
+                               l.smem, l.stream, p);
+        else
+            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_PRUNE, false, VEC>), g, b,
+                               l.smem, l.stream, p);
+    }
+    return hipGetLastError();
+}
+
+template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
+hipError_t bwd_one(const BwdParams &p, const Launch &l)
+{
+    hipLaunchKernelGGL((bwd_kernel<LPT, NCH, TIn, SCORE, VEC>), dim3(l.grid), dim3(kBlock), 0,
+                       l.stream, p);
+    return hipGetLastError();
+}
+
+// Launches the forward for the first listed N equal to nch.
+template <int LPT, bool VEC, int... N>
+bool fwd_pick(int nch, int dtype, int score, bool grouped, const FwdParams &p,
+              const Launch &l, hipError_t *err)
+{
+    auto one = [&](auto nc) {
+        constexpr int C = decltype(nc)::value;
+        if (dtype == 0)
+            *err = score == 0 ? fwd_one<LPT, C, float, 0, VEC>(p, grouped, l)
+                              : fwd_one<LPT, C, float, 1, VEC>(p, grouped, l);
+        else
+            *err = score == 0 ? fwd_one<LPT, C, uint16_t, 0, VEC>(p, grouped, l)
+                              : fwd_one<LPT, C, uint16_t, 1, VEC>(p, grouped, l);
+        return true;
+    };
+    return ((nch == N && one(std::integral_constant<int, N>{})) || ...);
+}
+
+template <int LPT, bool VEC, int... N>
+bool bwd_pick(int nch, int dtype, int score, const BwdParams &p, const Launch &l,
+              hipError_t *err)
+{
+    auto one = [&](auto nc) {
+        constexpr int C = decltype(nc)::value;
+        if (dtype == 0)
+            *err = score == 0 ? bwd_one<LPT, C, float, 0, VEC>(p, l)
+                              : bwd_one<LPT, C, float, 1, VEC>(p, l);
+        else
+            *err = score == 0 ? bwd_one<LPT, C, uint16_t, 0, VEC>(p, l)
+                              : bwd_one<LPT, C, uint16_t, 1, VEC>(p, l);
+        return true;
+    };
+    return ((nch == N && one(std::integral_constant<int, N>{})) || ...);
+}
+
+}  // namespace rker
+
+// Defines fwd_NAME / bwd_NAME for lane width LPT_, vector flag VEC_ and the
+// listed chunk counts.
+#define ROUTER_DEFINE_PART(NAME, LPT_, VEC_, ...)                                   \
+    namespace rker {                                                                \
+    bool fwd_##NAME(int lpt, int nch, bool vec, int dtype, int score, bool grouped, \
+                    const FwdParams &p, const Launch &l, hipError_t *err)           \
+    {                                                                               \
+        if (lpt != LPT_ || vec != VEC_)                                             \
+            return false;                                                           \
+        return fwd_pick<LPT_, VEC_, __VA_ARGS__>(nch, dtype, score, grouped, p, l,  \
+                                                 err);                              \
+    }                                                                               \
+    bool bwd_##NAME(int lpt, int nch, bool vec, int dtype, int score,               \
+                    const BwdParams &p, const Launch &l, hipError_t *err)           \
+    {                                                                               \
+        if (lpt != LPT_ || vec != VEC_)                                             \
+            return false;                                                           \
+        return bwd_pick<LPT_, VEC_, __VA_ARGS__>(nch, dtype, score, p, l, err);     \
+    }                                                                               \
+    }

@@ -1,0 +1,183 @@
+"""Helpers of the GPU parity tests: device transfer, the comparison rules,
+and one call that runs a workload through the HIP library and the fp64
+oracle on the same seeded inputs.
+
+Comparison rules (tolerances as stated for the router: fp32 rtol 2e-6 /
+atol 1e-7, bf16 rtol 1e-2):
+  * routing maps are compared bit for bit;
+  * where floating point decides the selection (expert bias or groups:
+    keys s + b and group sums), both sides decide in fp32, but the GPU's
+    fp32 score can differ from the correctly rounded one by an ulp; a token
+    whose oracle margin between the last kept and the first dropped
+    candidate is below NEAR_TIE is a near-tie token: its map must be a
+    valid selection up to NEAR_TIE and its weights consistent with that
+    selection, and such tokens are counted;
+  * values use |gpu - ref| <= atol + rtol |ref| (bf16: atol is 1e-2 times
+    the row's largest |ref|).
+"""
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from score_function_top_amd import router, synth  # noqa: E402
+
+DEV = "cuda:0"
+F32_RTOL, F32_ATOL = 2e-6, 1e-7
+BF16_RTOL = 1e-2
+NEAR_TIE = 2e-6
+SCORE_NAME = {synth.SOFTMAX: "softmax", synth.SIGMOID: "sigmoid"}
+
+
+def threads():
+    return int(os.environ.get("ORACLE_THREADS", min(16, os.cpu_count() or 1)))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(arr, dtype):
+    """Storage array (fp32, or bf16 bit patterns) -> device tensor."""
+    a = np.ascontiguousarray(arr)
+    if dtype == synth.F32:
+        return torch.from_numpy(a).to(DEV)
+    return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def f64(t):
+    if t.dtype == torch.bool:
+        return t.cpu().numpy().astype(np.uint8)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def tol_bad(gpu, ref, dtype, rtol=None, atol=None):
+    """Boolean mask of elements outside the tolerance."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if dtype == synth.F32:
+        rt = F32_RTOL if rtol is None else rtol
+        at = F32_ATOL if atol is None else atol
+        lim = at + rt * np.abs(ref)
+    else:
+        rt = BF16_RTOL if rtol is None else rtol
+        row = np.abs(ref).max(axis=-1, keepdims=True) if ref.ndim else np.abs(ref)
+        lim = rt * np.abs(ref) + rt * row
+    return ~(np.abs(gpu - ref) <= lim)
+
+
+def assert_close(gpu, ref, dtype, what, rows=None, rtol=None, atol=None):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if rows is not None:
+        gpu, ref = gpu[rows], ref[rows]
+    bad = tol_bad(gpu, ref, dtype, rtol, atol)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        worst = np.max(np.abs(gpu - ref))
+        raise AssertionError(
+            f"{what}: {bad.sum()} of {bad.size} elements outside tolerance, "
+            f"max |err| {worst:.3g}; first {idx.tolist()}: gpu "
+            f"{[gpu[tuple(i)] for i in idx]} ref {[ref[tuple(i)] for i in idx]}")
+
+
+def group_scores32(gv, G, q):
+    """fp32 sum of the q largest fp32 values of each group, largest first."""
+    T, E = gv.shape
+    g = np.sort(gv.reshape(T, G, E // G), axis=2)[:, :, ::-1][:, :, :q]
+    h = np.zeros((T, G), np.float32)
+    for i in range(q):
+        h = (h + g[:, :, i]).astype(np.float32)
+    return h.astype(np.float64)
+
+
+def check_near_tie(rows, gpu_map, gpu_probs, S, x64, wl, bias):
+    """Validity of the GPU's selection on near-tie rows (see module doc)."""
+    K, E = wl.K, wl.E
+    s32 = S[rows].astype(np.float32)
+    b = np.zeros(E, np.float32) if bias is None else bias.astype(np.float32)
+    gv = (s32 + b).astype(np.float32).astype(np.float64)
+    key = gv if bias is not None else x64[rows]
+    m = gpu_map[rows].astype(bool)
+    assert (m.sum(1) == K).all(), "near-tie rows must select K experts"
+    allowed = np.ones_like(m)
+    if wl.num_groups:
+        G, Kg = wl.num_groups, wl.group_topk
+        h = group_scores32(gv.astype(np.float32), G, K // Kg)
+        used = m.reshape(len(rows), G, E // G).any(axis=2)
+        assert (used.sum(1) <= Kg).all()
+        kth = -np.sort(-h, axis=1)[:, Kg - 1:Kg]
+        assert (h[used] >= np.broadcast_to(kth, h.shape)[used] - NEAR_TIE).all(), \
+            "near-tie rows must keep groups within NEAR_TIE of the best"
+        allowed = np.repeat(used, E // G, axis=1)
+    lo = np.where(m, key, np.inf).min(1)
+    hi = np.where(~m & allowed, key, -np.inf).max(1)
+    assert (lo >= hi - NEAR_TIE).all(), "near-tie selection violates the order"
+    # weights consistent with the chosen set
+    sref = S[rows]
+    denom = 1.0
+    if wl.renorm and (wl.score_fn == synth.SOFTMAX or K > 1):
+        denom = np.where(m, sref, 0.0).sum(1, keepdims=True)
+    want = np.where(m, wl.scaling_factor * sref / denom, 0.0)
+    assert_close(gpu_probs[rows], want, wl.dtype, "near-tie probs")
+
+
+def run_fwd(wl, T=None, check=True):
+    """Runs the topk forward of `wl` on the GPU and the oracle; checks the
+    outputs; returns a dict of the arrays used by later checks."""
+    x_st, x64 = wl.logits()
+    if T is not None:
+        x_st, x64 = x_st[:T], x64[:T]
+    bias = wl.bias()
+    say(f"[fwd] {wl.name} T={x64.shape[0]} E={wl.E} K={wl.K}")
+    xt = to_dev(x_st, wl.dtype)
+    bt = None if bias is None else torch.from_numpy(bias).to(DEV)
+    probs, rmap, inter = router.router_topk_fwd(
+        xt, wl.K, SCORE_NAME[wl.score_fn], wl.renorm, wl.num_groups, wl.group_topk,
+        wl.scaling_factor, bt)
+    torch.cuda.synchronize()
+    P, M, S, margin = oracle.topk_fwd(
+        x64, wl.K, wl.score_fn, wl.renorm, wl.num_groups, wl.group_topk,
+        wl.scaling_factor, None if bias is None else bias.astype(np.float64),
+        threads=threads())
+    out = dict(x_st=x_st, x64=x64, xt=xt, bias=bias, probs=probs, map=rmap,
+               inter=inter, P=P, M=M, S=S, margin=margin, near=np.zeros(0, int))
+    if not check:
+        return out
+    gp, gm, gi = f64(probs), f64(rmap), f64(inter)
+    assert_close(gi, S, synth.F32, f"{wl.name} intermediate")
+    computed_keys = bias is not None or wl.num_groups > 0
+    near = np.nonzero(margin < NEAR_TIE)[0] if computed_keys else np.zeros(0, int)
+    exact = np.setdiff1d(np.arange(x64.shape[0]), near)
+    diff = np.nonzero((gm[exact] != M[exact]).any(1))[0]
+    assert diff.size == 0, (f"{wl.name}: routing map differs on {diff.size} rows, "
+                            f"first {exact[diff[:5]].tolist()}")
+    assert_close(gp, P, wl.dtype, f"{wl.name} probs", rows=exact)
+    if near.size:
+        check_near_tie(near, gm, gp, S, x64, wl, bias)
+        assert near.size <= max(8, x64.shape[0] // 100), f"{near.size} near-tie rows"
+    out["near"] = near
+    say(f"   ok; near-tie rows {near.size}")
+    return out
+
+
+def run_aux_fwd(wl, T=None):
+    x_st, x64 = wl.logits()
+    if T is not None:
+        x_st, x64 = x_st[:T], x64[:T]
+    say(f"[aux fwd] {wl.name} T={x64.shape[0]} E={wl.E} K={wl.K}")
+    xt = to_dev(x_st, wl.dtype)
+    sc, rmap, inter = router.router_aux_scores(xt, wl.K, SCORE_NAME[wl.score_fn],
+                                               wl.aux_renorm)
+    torch.cuda.synchronize()
+    A, M, S = oracle.aux_fwd(x64, wl.K, wl.score_fn, wl.aux_renorm, threads=threads())
+    assert (f64(rmap) == M).all(), f"{wl.name}: aux routing map differs"
+    assert_close(f64(inter), S, synth.F32, f"{wl.name} aux intermediate")
+    assert_close(f64(sc), A, wl.dtype, f"{wl.name} aux scores")
+    return dict(x64=x64, xt=xt, scores=sc, map=rmap, inter=inter, A=A, M=M, S=S)

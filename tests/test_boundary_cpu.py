@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/router.h declares, and rejects bad arguments on the host before
+any HIP call (no GPU needed: nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from score_function_top_amd import router
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "router.h")
+
+OK, INV, OVF, UNS = router.OK, router.ERR_INVALID_ARG, router.ERR_OVERFLOW, router.ERR_UNSUPPORTED
+P = 0x100000  # a 16-byte aligned fake device address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(router_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = router.load()
+    names = declared_functions()
+    assert {"router_topk_fwd", "router_topk_bwd", "router_aux_scores",
+            "router_aux_scores_bwd", "router_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s, key in ((OK, "ROUTER_OK"), (INV, "INVALID_ARG"), (OVF, "OVERFLOW"),
+                   (UNS, "UNSUPPORTED"), (router.ERR_HIP, "ERR_HIP")):
+        assert key in router.status_str(s)
+    assert "unknown" in router.status_str(99)
+
+
+def fwd(**kw):
+    a = dict(logits=P, dtype=0, T=8, E=16, K=2, score=0, renorm=0, G=0, Kg=0,
+             c=1.0, bias=None, probs=P, map=P, inter=P, stream=None)
+    a.update(kw)
+    return router.load().router_topk_fwd(
+        a["logits"], a["dtype"], a["T"], a["E"], a["K"], a["score"], a["renorm"],
+        a["G"], a["Kg"], a["c"], a["bias"], a["probs"], a["map"], a["inter"],
+        a["stream"])
+
+
+def bwd(**kw):
+    a = dict(g=P, s=P, m=P, dtype=0, T=8, E=16, K=2, score=0, renorm=0, c=1.0,
+             dx=P, stream=None)
+    a.update(kw)
+    return router.load().router_topk_bwd(
+        a["g"], a["s"], a["m"], a["dtype"], a["T"], a["E"], a["K"], a["score"],
+        a["renorm"], a["c"], a["dx"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), INV), (dict(dtype=-1), INV), (dict(score=2), INV),
+    (dict(T=-1), INV), (dict(E=0), INV), (dict(K=0), INV), (dict(K=17), INV),
+    (dict(E=4097, K=2), UNS), (dict(T=1 << 62), OVF),
+    (dict(G=3), INV),                          # 16 % 3 != 0
+    (dict(G=4, Kg=0), INV), (dict(G=4, Kg=5), INV),
+    (dict(G=4, Kg=2, K=3), INV),               # K % Kg != 0
+    (dict(G=8, Kg=1, K=4), INV),               # K/Kg = 4 > E/G = 2
+    (dict(G=-1), INV),
+    (dict(c=float("inf")), INV), (dict(c=float("nan")), INV),
+    (dict(bias=P), UNS),                       # bias with softmax
+    (dict(logits=None), INV), (dict(probs=None), INV), (dict(map=None), INV),
+    (dict(inter=None), INV),
+    (dict(logits=P + 2), INV),                 # fp32 array not 4-byte aligned
+    (dict(inter=P + 1), INV), (dict(dtype=1, logits=P + 1), INV),
+    (dict(score=1, bias=P + 2), INV),
+    (dict(T=0), OK),                           # valid no-op, nothing launched
+    (dict(T=0, logits=None, probs=None, map=None, inter=None), OK),
+])
+def test_topk_fwd_host_checks(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), INV), (dict(score=-1), INV), (dict(T=-2), INV), (dict(E=0), INV),
+    (dict(K=0), INV), (dict(K=17), INV), (dict(E=5000, K=2), UNS),
+    (dict(T=1 << 62), OVF), (dict(c=float("-inf")), INV),
+    (dict(g=None), INV), (dict(s=None), INV), (dict(m=None), INV), (dict(dx=None), INV),
+    (dict(s=P + 2), INV), (dict(dtype=1, dx=P + 1), INV),
+    (dict(T=0), OK), (dict(T=0, g=None, s=None, m=None, dx=None), OK),
+])
+def test_topk_bwd_host_checks(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_aux_host_checks():
+    lib = router.load()
+    f = lib.router_aux_scores
+    assert f(P, 0, 4, 16, 0, 0, 1, P, P, P, None) == INV
+    assert f(P, 0, 4, 16, 17, 0, 1, P, P, P, None) == INV
+    assert f(P, 0, 4, 16, 2, 5, 1, P, P, P, None) == INV
+    assert f(None, 0, 4, 16, 2, 0, 1, P, P, P, None) == INV
+    assert f(None, 0, 0, 16, 2, 0, 1, None, None, None, None) == OK
+    b = lib.router_aux_scores_bwd
+    assert b(P, P, 0, -1, 16, 0, 1, P, None) == INV
+    assert b(P, P, 0, 4, 0, 0, 1, P, None) == INV
+    assert b(None, P, 0, 4, 16, 0, 1, P, None) == INV
+    assert b(P, P, 0, 4, 5000, 1, 1, P, None) == UNS
+    assert b(None, None, 0, 0, 16, 0, 1, None, None) == OK
+
+
+def test_threshold_setter():
+    old = router.get_topk_path_threshold()
+    try:
+        router.set_topk_path_threshold(0)
+        assert router.get_topk_path_threshold() == 0
+        router.set_topk_path_threshold(64)
+        assert router.get_topk_path_threshold() == 64
+        for bad in (-1, 4097):
+            with pytest.raises(router.RouterError) as e:
+                router.set_topk_path_threshold(bad)
+            assert e.value.status == INV
+    finally:
+        router.set_topk_path_threshold(old)
+
+
+@pytest.mark.parametrize("env,expect", [(None, 8), ("3", 3), ("0", 0), ("abc", 8),
+                                        ("-4", 8), ("5000", 8), ("12x", 8)])
+def test_threshold_environment(env, expect):
+    code = ("from score_function_top_amd import router;"
+            "print(router.get_topk_path_threshold())")
+    e = dict(os.environ)
+    e.pop("ROUTER_TOPK_PATH_THRESHOLD", None)
+    if env is not None:
+        e["ROUTER_TOPK_PATH_THRESHOLD"] = env
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=e,
+                         capture_output=True, text=True, check=True).stdout
+    assert int(out.strip()) == expect
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        router.router_topk_fwd(x, 2)
+    with pytest.raises(ValueError):
+        router.router_aux_scores(x, 2)
+    with pytest.raises(ValueError):
+        router.router_topk_bwd(x, x, x.bool(), 2)

@@ -1,0 +1,359 @@
+"""GPU parity: the HIP router library (through its C ABI) against the fp64
+oracle on the same seeded inputs.  Needs an MI355X and a built
+librouter.so; every case prints its name before touching the GPU."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_support import (DEV, SCORE_NAME, assert_close, f64, run_aux_fwd, run_fwd, say,
+                         threads, to_dev)
+from score_function_top_amd import router, synth
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    router.load()
+    yield
+    router.set_topk_path_threshold(8)
+
+
+def wl_variant(base, **kw):
+    return dataclasses.replace(base, **kw)
+
+
+def grads(wl, T, aux=False):
+    st, g64 = wl.aux_grad() if aux else wl.grad()
+    return st[:T], g64[:T]
+
+
+# ------------------------------------------------------------ workloads
+
+@pytest.mark.parametrize("name", list(WL))
+def test_workload_forward(name):
+    run_fwd(WL[name])
+
+
+@pytest.mark.parametrize("name", list(WL))
+def test_workload_backward_isolated(name):
+    """GPU and oracle backward on identical inputs: the oracle's forward
+    intermediate (rounded to fp32) and map, and seeded gradients."""
+    wl = WL[name]
+    _, x64 = wl.logits()
+    bias = wl.bias()
+    say(f"[bwd isolated] {name}")
+    _, M, S, _ = oracle.topk_fwd(x64, wl.K, wl.score_fn, wl.renorm, wl.num_groups,
+                                 wl.group_topk, wl.scaling_factor,
+                                 None if bias is None else bias.astype(np.float64),
+                                 threads=threads())
+    g_st, g64 = grads(wl, wl.T)
+    if wl.grad_on_map:
+        g64 = g64 * M
+        if wl.dtype == synth.F32:
+            g_st = (g_st * M).astype(np.float32)
+        else:
+            g_st = np.where(M.astype(bool), g_st, np.uint16(0)).astype(np.uint16)
+    s32 = S.astype(np.float32)
+    dx = router.router_topk_bwd(to_dev(g_st, wl.dtype), torch.from_numpy(s32).to(DEV),
+                                torch.from_numpy(M.astype(bool)).to(DEV), wl.K,
+                                SCORE_NAME[wl.score_fn], wl.renorm, wl.scaling_factor)
+    torch.cuda.synchronize()
+    ref = oracle.topk_bwd(g64, s32.astype(np.float64), M, wl.K, wl.score_fn, wl.renorm,
+                          wl.scaling_factor, threads=threads())
+    assert_close(f64(dx), ref, wl.dtype, f"{name} grad_logits")
+
+
+@pytest.mark.parametrize("name", list(WL))
+def test_workload_backward_chained(name):
+    """x -> fwd -> bwd on each side; rows whose maps agree are compared."""
+    wl = WL[name]
+    r = run_fwd(wl, check=False)
+    g_st, g64 = grads(wl, wl.T)
+    say(f"[bwd chained] {name}")
+    dx = router.router_topk_bwd(to_dev(g_st, wl.dtype), r["inter"], r["map"], wl.K,
+                                SCORE_NAME[wl.score_fn], wl.renorm, wl.scaling_factor)
+    torch.cuda.synchronize()
+    ref = oracle.topk_bwd(g64, r["S"], r["M"], wl.K, wl.score_fn, wl.renorm,
+                          wl.scaling_factor, threads=threads())
+    same = np.nonzero((f64(r["map"]) == r["M"]).all(1))[0]
+    assert same.size >= wl.T - max(8, wl.T // 100)
+    assert_close(f64(dx), ref, wl.dtype, f"{name} chained grad", rows=same,
+                 rtol=1e-5 if wl.dtype == synth.F32 else None)
+
+
+@pytest.mark.parametrize("name", [n for n in WL if WL[n].aux])
+def test_workload_aux(name):
+    wl = WL[name]
+    r = run_aux_fwd(wl)
+    g_st, g64 = grads(wl, wl.T, aux=True)
+    say(f"[aux bwd] {name}")
+    s32 = r["S"].astype(np.float32)
+    dx = router.router_aux_scores_bwd(to_dev(g_st, wl.dtype), torch.from_numpy(s32).to(DEV),
+                                      SCORE_NAME[wl.score_fn], wl.aux_renorm)
+    dxc = router.router_aux_scores_bwd(to_dev(g_st, wl.dtype), r["inter"],
+                                       SCORE_NAME[wl.score_fn], wl.aux_renorm)
+    torch.cuda.synchronize()
+    ref = oracle.aux_bwd(g64, s32.astype(np.float64), wl.score_fn, wl.aux_renorm,
+                         threads=threads())
+    assert_close(f64(dx), ref, wl.dtype, f"{name} aux grad")
+    refc = oracle.aux_bwd(g64, r["S"], wl.score_fn, wl.aux_renorm, threads=threads())
+    assert_close(f64(dxc), refc, wl.dtype, f"{name} aux chained grad", rtol=1e-5)
+
+
+# ------------------------------------------------------------ E/K sweep
+
+SWEEP = [(E, K, sf) for E in (256, 512, 2304) for K in (4, 8, 22, 36) if K <= E
+         for sf in (synth.SOFTMAX, synth.SIGMOID)]
+
+
+@pytest.mark.parametrize("E,K,sf", SWEEP)
+def test_sweep(E, K, sf):
+    """T=8192 E/K grid at a ragged T=1031 slice: fwd, bwd, aux fwd/bwd."""
+    wl = synth.sweep_workload(E, K, sf)
+    T = 1031
+    r = run_fwd(wl, T=T)
+    g_st, g64 = grads(wl, T)
+    dx = router.router_topk_bwd(to_dev(g_st, wl.dtype), r["inter"], r["map"], K,
+                                SCORE_NAME[sf], wl.renorm, wl.scaling_factor)
+    torch.cuda.synchronize()
+    ref = oracle.topk_bwd(g64, r["S"], r["M"], K, sf, wl.renorm, wl.scaling_factor,
+                          threads=threads())
+    assert_close(f64(dx), ref, wl.dtype, f"{wl.name} grad", rtol=1e-5)
+    a = run_aux_fwd(wl, T=T)
+    dxa = router.router_aux_scores_bwd(to_dev(g_st, wl.dtype), a["inter"], SCORE_NAME[sf],
+                                       wl.aux_renorm)
+    torch.cuda.synchronize()
+    refa = oracle.aux_bwd(g64, a["S"], sf, wl.aux_renorm, threads=threads())
+    assert_close(f64(dxa), refa, wl.dtype, f"{wl.name} aux grad", rtol=1e-5)
+
+
+# ------------------------------------------------------------ edge shapes
+
+def edge_wl(T, E, K, sf, renorm=False, bias=0.0, G=0, Kg=0, dtype=synth.F32, c=1.0,
+            seed=7):
+    return synth.Workload(name=f"edge_T{T}_E{E}_K{K}_{SCORE_NAME[sf]}_r{int(renorm)}"
+                          f"_b{bias}_G{G}_{'bf16' if dtype else 'f32'}",
+                          T=T, E=E, K=K, score_fn=sf, renorm=renorm, num_groups=G,
+                          group_topk=Kg, scaling_factor=c, dtype=dtype, bias_range=bias,
+                          seed_logits=seed, seed_grad=seed + 1, seed_bias=seed + 2,
+                          seed_aux_grad=seed + 3)
+
+
+EDGE = [
+    (1, 16, 2, synth.SOFTMAX), (65, 16, 16, synth.SOFTMAX), (8193, 64, 8, synth.SIGMOID),
+    (33, 1, 1, synth.SOFTMAX), (33, 1, 1, synth.SIGMOID), (70, 3, 2, synth.SOFTMAX),
+    (70, 3, 3, synth.SIGMOID), (129, 100, 7, synth.SOFTMAX), (129, 100, 100, synth.SIGMOID),
+    (77, 257, 9, synth.SOFTMAX), (77, 257, 40, synth.SIGMOID), (50, 4096, 36, synth.SOFTMAX),
+    (50, 4096, 1, synth.SIGMOID), (40, 4096, 100, synth.SOFTMAX), (31, 2304, 64, synth.SOFTMAX),
+    (31, 2304, 65, synth.SOFTMAX), (19, 2000, 2000, synth.SOFTMAX), (300, 512, 33, synth.SIGMOID),
+    (300, 256, 17, synth.SOFTMAX), (300, 128, 64, synth.SOFTMAX),
+]
+
+
+@pytest.mark.parametrize("T,E,K,sf", EDGE)
+@pytest.mark.parametrize("renorm", [False, True])
+def test_edge_shapes(T, E, K, sf, renorm):
+    wl = edge_wl(T, E, K, sf, renorm, c=1.5)
+    r = run_fwd(wl)
+    g_st, g64 = grads(wl, T)
+    dx = router.router_topk_bwd(to_dev(g_st, wl.dtype), r["inter"], r["map"], K,
+                                SCORE_NAME[sf], renorm, 1.5)
+    torch.cuda.synchronize()
+    ref = oracle.topk_bwd(g64, r["S"], r["M"], K, sf, renorm, 1.5, threads=threads())
+    assert_close(f64(dx), ref, synth.F32, f"{wl.name} grad", rtol=1e-5)
+
+
+@pytest.mark.parametrize("T,E,K,G,Kg,dtype", [
+    (500, 256, 8, 8, 4, synth.BF16), (300, 256, 8, 8, 4, synth.F32), (200, 64, 6, 4, 2, synth.F32),
+    (129, 512, 22, 16, 11, synth.F32), (64, 2304, 36, 36, 6, synth.F32),
+    (90, 96, 12, 12, 4, synth.F32), (70, 160, 9, 10, 3, synth.F32), (50, 256, 8, 64, 8, synth.F32),
+])
+@pytest.mark.parametrize("biased", [False, True])
+def test_groups(T, E, K, G, Kg, dtype, biased):
+    wl = edge_wl(T, E, K, synth.SIGMOID, True, bias=0.05 if biased else 0.0, G=G, Kg=Kg,
+                 dtype=dtype, c=2.5, seed=11)
+    run_fwd(wl)
+
+
+def test_grouped_softmax():
+    run_fwd(edge_wl(300, 256, 8, synth.SOFTMAX, True, G=8, Kg=4, seed=13))
+
+
+def test_bf16_paths():
+    for sf in (synth.SOFTMAX, synth.SIGMOID):
+        for E, K in ((256, 4), (512, 22), (2304, 36), (100, 5)):
+            wl = edge_wl(257, E, K, sf, sf == synth.SIGMOID, dtype=synth.BF16, seed=17)
+            r = run_fwd(wl)
+            g_st, g64 = grads(wl, 257)
+            dx = router.router_topk_bwd(to_dev(g_st, wl.dtype), r["inter"], r["map"], K,
+                                        SCORE_NAME[sf], wl.renorm, 1.0)
+            torch.cuda.synchronize()
+            ref = oracle.topk_bwd(g64, r["S"], r["M"], K, sf, wl.renorm, 1.0,
+                                  threads=threads())
+            assert_close(f64(dx), ref, synth.BF16, f"{wl.name} grad")
+            run_aux_fwd(wl, T=257)
+
+
+# ------------------------------------------------------------ ties
+
+def _tie_case(x64, K, sf, renorm, dtype=synth.F32):
+    if dtype == synth.F32:
+        st = x64.astype(np.float32)
+    else:
+        st = synth.f32_to_bf16_bits(x64.astype(np.float32))
+        x64 = synth.bf16_bits_to_f32(st).astype(np.float64)
+    xt = to_dev(st, dtype)
+    p, m, i = router.router_topk_fwd(xt, K, SCORE_NAME[sf], renorm)
+    a, am, ai = router.router_aux_scores(xt, K, SCORE_NAME[sf], renorm)
+    torch.cuda.synchronize()
+    P, M, S, _ = oracle.topk_fwd(x64, K, sf, renorm, threads=threads())
+    A, AM, AS = oracle.aux_fwd(x64, K, sf, renorm, threads=threads())
+    assert (f64(m) == M).all() and (f64(am) == AM).all()
+    assert_close(f64(p), P, dtype, "tie probs")
+    assert_close(f64(a), A, dtype, "tie aux scores")
+
+
+@pytest.mark.parametrize("E,K", [(16, 2), (256, 4), (256, 8), (512, 22), (2304, 36),
+                                 (2304, 4), (100, 50)])
+def test_ties(E, K):
+    say(f"[ties] E={E} K={K}")
+    rng = np.random.default_rng(E + K)
+    T = 300
+    x = np.zeros((T, E))
+    x[1] = 1.5                                         # all equal
+    x[2:100] = rng.integers(-3, 4, (98, E))            # heavy ties everywhere
+    x[100:200] = rng.integers(0, 2, (100, E)) * 0.5    # two values only
+    x[200:] = np.round(rng.normal(0, 1, (T - 200, E)), 1)
+    x[3, :] = -0.0                                      # signed zeros tie
+    x[3, 1::2] = 0.0
+    for sf in (synth.SOFTMAX, synth.SIGMOID):
+        for renorm in (False, True):
+            _tie_case(x, K, sf, renorm)
+            _tie_case(x, K, sf, renorm, synth.BF16)
+
+
+# ------------------------------------------------------------ paths
+
+PATH_CASES = [(512, 2304, 36, synth.SOFTMAX, 0.0, 0), (700, 256, 4, synth.SOFTMAX, 0.0, 0),
+              (700, 512, 22, synth.SIGMOID, 0.1, 0), (300, 256, 8, synth.SIGMOID, 0.05, 8),
+              (300, 100, 30, synth.SOFTMAX, 0.0, 0), (90, 2304, 8, synth.SIGMOID, 0.0, 0)]
+
+
+@pytest.mark.parametrize("T,E,K,sf,b,G", PATH_CASES)
+def test_path_parity(T, E, K, sf, b, G):
+    """Every selection path gives the same map and bit-identical weights."""
+    wl = edge_wl(T, E, K, sf, True, bias=b, G=G, Kg=4 if G else 0, c=2.0, seed=23)
+    outs = []
+    try:
+        for thr in (0, 8, 4096):
+            router.set_topk_path_threshold(thr)
+            r = run_fwd(wl, check=(thr == 8))
+            outs.append((f64(r["probs"]), f64(r["map"]), f64(r["inter"])))
+    finally:
+        router.set_topk_path_threshold(8)
+    for o in outs[1:]:
+        assert (o[1] == outs[0][1]).all(), "maps differ between paths"
+        assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[2], outs[0][2])
+
+
+def test_deterministic():
+    wl = WL["c4_softmax_2304x36"]
+    x_st, _ = wl.logits()
+    xt = to_dev(x_st[:2048], wl.dtype)
+    say("[determinism] c4 slice")
+    a = router.router_topk_fwd(xt, wl.K)
+    b = router.router_topk_fwd(xt, wl.K)
+    g = torch.randn(xt.shape, device=DEV, generator=torch.Generator(DEV).manual_seed(5))
+    da = router.router_topk_bwd(g, a[2], a[1], wl.K)
+    db = router.router_topk_bwd(g, b[2], b[1], wl.K)
+    torch.cuda.synchronize()
+    for u, v in zip((*a, da), (*b, db)):
+        assert torch.equal(u, v)
+
+
+# ------------------------------------------------------------ layouts
+
+@pytest.mark.parametrize("E,K,sf", [(256, 4, synth.SOFTMAX), (2304, 36, synth.SOFTMAX),
+                                    (512, 22, synth.SIGMOID)])
+def test_unaligned_views(E, K, sf):
+    """Arrays offset by one element take the element-wise kernels."""
+    wl = edge_wl(133, E, K, sf, sf == synth.SIGMOID, c=1.25, seed=29)
+    x_st, x64 = wl.logits()
+    say(f"[unaligned] {wl.name}")
+    n = x64.size
+    buf = torch.empty(n + 1, dtype=torch.float32, device=DEV)
+    buf[1:] = torch.from_numpy(x_st.reshape(-1)).to(DEV)
+    xt = buf[1:].view(133, E)
+    outs = [torch.empty(n + 1, dtype=dt, device=DEV)[1:].view(133, E)
+            for dt in (torch.float32, torch.bool, torch.float32)]
+    p, m, i = router.router_topk_fwd(xt, K, SCORE_NAME[sf], wl.renorm, scaling_factor=1.25,
+                                     out=outs)
+    g = torch.empty(n + 1, dtype=torch.float32, device=DEV)[1:].view(133, E)
+    g_st, g64 = wl.grad()
+    g.copy_(torch.from_numpy(g_st))
+    dx = router.router_topk_bwd(g, i, m, K, SCORE_NAME[sf], wl.renorm, 1.25,
+                                out=torch.empty(n + 1, device=DEV)[1:].view(133, E))
+    torch.cuda.synchronize()
+    P, M, S, _ = oracle.topk_fwd(x64, K, sf, wl.renorm, scaling_factor=1.25, threads=threads())
+    assert (f64(m) == M).all()
+    assert_close(f64(p), P, synth.F32, "unaligned probs")
+    assert_close(f64(i), S, synth.F32, "unaligned intermediate")
+    ref = oracle.topk_bwd(g64, S, M, K, sf, wl.renorm, 1.25, threads=threads())
+    assert_close(f64(dx), ref, synth.F32, "unaligned grad", rtol=1e-5)
+
+
+def test_zero_tokens():
+    x = torch.empty(0, 64, device=DEV)
+    p, m, i = router.router_topk_fwd(x, 4)
+    dx = router.router_topk_bwd(x, i, m, 4)
+    a = router.router_aux_scores(x, 4)
+    da = router.router_aux_scores_bwd(x, i)
+    torch.cuda.synchronize()
+    assert p.shape == (0, 64) and dx.shape == (0, 64) and a[0].shape == (0, 64)
+    assert da.shape == (0, 64)
+
+
+def test_side_stream():
+    wl = WL["c2_softmax_256x4"]
+    x_st, x64 = wl.logits()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xt = to_dev(x_st[:1000], wl.dtype)
+        p, m, i = router.router_topk_fwd(xt, wl.K)
+    s.synchronize()
+    P, M, S, _ = oracle.topk_fwd(x64[:1000], wl.K, threads=threads())
+    assert (f64(m) == M).all()
+    assert_close(f64(p), P, synth.F32, "side-stream probs")
+
+
+def test_beyond_32bit_elements():
+    """T*E > 2^31 elements: sampled rows against the oracle."""
+    E, K = 256, 8
+    T = (1 << 31) // E + 4099
+    say(f"[large] T={T} E={E}")
+    gen = torch.Generator(DEV).manual_seed(31)
+    x = torch.randn(T, E, device=DEV, generator=gen)
+    p, m, i = router.router_topk_fwd(x, K, "sigmoid", True, scaling_factor=2.0)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+                                     np.random.default_rng(3).integers(0, T, 200)]))
+    rt = torch.from_numpy(rows).to(DEV)
+    x64 = f64(x[rt])
+    P, M, S, _ = oracle.topk_fwd(x64, K, synth.SIGMOID, True, scaling_factor=2.0)
+    assert (f64(m[rt]) == M).all()
+    assert_close(f64(p[rt]), P, synth.F32, "large probs")
+    assert_close(f64(i[rt]), S, synth.F32, "large intermediate")
+    g = torch.randn(T, E, device=DEV, generator=gen)
+    del x
+    dx = router.router_topk_bwd(g, i, m, K, "sigmoid", True, 2.0)
+    torch.cuda.synchronize()
+    ref = oracle.topk_bwd(f64(g[rt]), f64(i[rt]), f64(m[rt]), K, synth.SIGMOID, True, 2.0)
+    assert_close(f64(dx[rt]), ref, synth.F32, "large grad")

@@ -1,0 +1,289 @@
+"""Benchmark of the fused MoE router on one MI355X.
+
+One step = one pass of the whole router hot path over one batch: the top-k
+forward (score function + selection + dense probs / routing map /
+intermediate), the top-k backward, the aux-loss score forward and its
+backward, on the headline workload (T=8192 tokens, E=2304 experts, K=36,
+fp32 softmax logits ~ N(0, std 2)).
+
+Throughput is effective bandwidth, counted as in the fused-router page's
+"Performance" paragraph ("[Common] Optimize fused router forward/backward
+kernels", NVIDIA TransformerEngine pull request 3012): the minimum bytes a
+kernel must move (read its inputs once, write its outputs once) divided by
+its time.  Algorithmic bytes per element: forward 13 (fp32 logits + probs,
+1-byte map, fp32 intermediate), backward 13, aux forward 13, aux backward
+12.  `value` = all bytes of a step / step time.
+
+Inputs are resident in HBM before the timed region.  Every kernel reads
+buffers last touched several kernels earlier: the step's kernels use
+different sets out of >= 2 GiB of rotating buffer sets, so neither the
+L2 nor the 256 MB Infinity Cache holds them (pass --warm to reuse one set).
+
+Prints one JSON line.  --gpus above 1 exits: this router is benchmarked on
+one GPU.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s (and % of 8 TB/s) for router fwd/bwd at T=8192, E/K sweep"
+PEAK_GBPS = 8000.0          # MI355X HBM3E
+BYTES_PER_ELEM = {"topk_fwd": 13, "topk_bwd": 13, "aux_fwd": 13, "aux_bwd": 12}
+BF16_BYTES_PER_ELEM = {"topk_fwd": 9, "topk_bwd": 9, "aux_fwd": 9, "aux_bwd": 8}
+# Kernel symbol prefixes as they appear in profiler traces.
+KERNEL_SYMBOL = {"topk_fwd": "fwd_kernel", "topk_bwd": "bwd_kernel",
+                 "aux_fwd": "fwd_kernel", "aux_bwd": "bwd_kernel"}
+# B300 figures of the fused-router page for this exact shape (context only).
+PAGE_B300_GBPS = {"topk_fwd": 964, "topk_bwd": 2766, "aux_fwd": 891, "aux_bwd": 4201}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "score_function_top_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """Measured HBM bytes per launch of `kernel` from the committed profiler
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_c4_2304x36.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, tokens):
+    """The fp64 oracle (as it stands) over the first `tokens` tokens of the
+    workload, all four passes, on this host's cores."""
+    import numpy as np
+    import oracle
+    thr = max(1, min(os.cpu_count() or 1, 64))
+    x_st, x64 = wl.logits()
+    g_st, g64 = wl.grad()
+    a_st, a64 = wl.aux_grad()
+    x64, g64, a64 = x64[:tokens], g64[:tokens], a64[:tokens]
+    t0 = time.perf_counter()
+    P, M, S, _ = oracle.topk_fwd(x64, wl.K, wl.score_fn, wl.renorm, threads=thr)
+    oracle.topk_bwd(g64, S, M, wl.K, wl.score_fn, wl.renorm, wl.scaling_factor, threads=thr)
+    A, AM, AS = oracle.aux_fwd(x64, wl.K, wl.score_fn, wl.aux_renorm, threads=thr)
+    oracle.aux_bwd(a64, AS, wl.score_fn, wl.aux_renorm, threads=thr)
+    dt = time.perf_counter() - t0
+    bytes_ = tokens * wl.E * sum(BYTES_PER_ELEM.values())
+    del P, A, AM, np
+    return {"value": round(bytes_ / dt / 1e9, 3), "unit": "GB/s", "cores": thr,
+            "kind": "oracle",
+            "sample": f"first {tokens} of {wl.T} tokens of the workload, all four passes "
+                      f"(topk fwd, topk bwd, aux fwd, aux bwd), fp64 C oracle, "
+                      f"{dt:.2f} s wall, same byte formula as the GPU value"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c4_softmax_2304x36")
+    ap.add_argument("--warm", action="store_true", help="reuse one buffer set")
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="oracle sample size in tokens (0: the whole batch)")
+    ap.add_argument("--only", choices=["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"],
+                    help="time only this kernel kind (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also time a plain device copy of this size (profiler scale)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.exit("bench.py: the router is benchmarked on one GPU; multi-GPU runs "
+                 "(--gpus > 1) are not part of this build")
+
+    import numpy as np
+    import torch
+    from score_function_top_amd import router, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, E, K = wl.T, wl.E, wl.K
+    sname = "softmax" if wl.score_fn == synth.SOFTMAX else "sigmoid"
+    tdt = torch.float32 if wl.dtype == synth.F32 else torch.bfloat16
+    esz = 4 if wl.dtype == synth.F32 else 2
+
+    # ---- inputs: seeded on the host once, copied into every buffer set
+    def host(arr):
+        a = np.ascontiguousarray(arr)
+        if wl.dtype == synth.F32:
+            return torch.from_numpy(a)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+
+    x_h = host(wl.logits()[0])
+    g_h = host(wl.grad()[0])
+    a_h = host(wl.aux_grad()[0])
+    bias = wl.bias()
+    bias_d = None if bias is None else torch.from_numpy(bias).to(dev)
+    set_bytes = T * E * (esz * 6 + 4 * 2 + 1 * 2) + T * E * esz  # 11 arrays per set
+    n_sets = 1 if args.warm else (args.sets or max(4, -(-(2 << 30) // set_bytes)))
+
+    def new_set():
+        s = {k: torch.empty(T, E, dtype=tdt, device=dev)
+             for k in ("x", "probs", "g", "dx", "ascores", "ag", "adx")}
+        s.update({k: torch.empty(T, E, dtype=torch.float32, device=dev)
+                  for k in ("inter", "ainter")})
+        s.update({k: torch.empty(T, E, dtype=torch.bool, device=dev)
+                  for k in ("map", "amap")})
+        s["x"].copy_(x_h)
+        s["g"].copy_(g_h)
+        s["ag"].copy_(a_h)
+        return s
+
+    sets = [new_set() for _ in range(n_sets)]
+
+    def launch(kind, s):
+        if kind == "topk_fwd":
+            router.router_topk_fwd(s["x"], K, sname, wl.renorm, wl.num_groups, wl.group_topk,
+                                   wl.scaling_factor, bias_d,
+                                   out=(s["probs"], s["map"], s["inter"]))
+        elif kind == "topk_bwd":
+            router.router_topk_bwd(s["g"], s["inter"], s["map"], K, sname, wl.renorm,
+                                   wl.scaling_factor, out=s["dx"])
+        elif kind == "aux_fwd":
+            router.router_aux_scores(s["x"], K, sname, wl.aux_renorm,
+                                     out=(s["ascores"], s["amap"], s["ainter"]))
+        else:
+            router.router_aux_scores_bwd(s["ag"], s["ainter"], sname, wl.aux_renorm,
+                                         out=s["adx"])
+
+    all_kinds = ["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"]
+    kinds = [args.only] if args.only else all_kinds
+    # kernel k of step i works on set (i + k) % n: with n >= 4 every input was
+    # last touched a full rotation of other buffers earlier (the backward
+    # passes read the forward outputs of earlier steps)
+    for s in sets:                       # produce every set's forward outputs
+        launch("topk_fwd", s)
+        launch("aux_fwd", s)
+    torch.cuda.synchronize()
+
+    def step(i):
+        for kind in kinds:
+            launch(kind, sets[(i + all_kinds.index(kind)) % n_sets])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, one event pair around them
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+
+    # ---- per-kernel average launch duration: K back-to-back launches of one
+    # kind (rotating sets, as in the step), one event pair around them
+    per_kernel_us = {}
+    for kind in kinds:
+        k0 = all_kinds.index(kind)
+        for i in range(3):
+            launch(kind, sets[(i + k0) % n_sets])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(args.steps):
+            launch(kind, sets[(i + k0) % n_sets])
+        b.record()
+        torch.cuda.synchronize()
+        per_kernel_us[kind] = a.elapsed_time(b) * 1e3 / args.steps
+
+    bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
+    kern = {}
+    for kind in kinds:
+        nbytes = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None) else 0)
+        avg = per_kernel_us[kind]
+        kern[kind] = {"us_avg": round(avg, 2), "algo_bytes": nbytes,
+                      "GBps": round(nbytes / avg / 1e3, 1),
+                      "frac_of_peak": round(nbytes / avg / 1e3 / PEAK_GBPS, 4)}
+        if args.workload == "c4_softmax_2304x36":
+            kern[kind]["page_b300_GBps_context"] = PAGE_B300_GBPS[kind]
+    step_bytes = sum(k["algo_bytes"] for k in kern.values())
+    ms_per_step = total_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    dom = max(kinds, key=lambda k: kern[k]["us_avg"])
+    traffic = read_traffic(dom) if args.workload == "c4_softmax_2304x36" and not args.warm else None
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["GBps"], "peak": PEAK_GBPS,
+            "unit": "GB/s", "frac": round(kern[dom]["GBps"] / PEAK_GBPS, 4),
+            "traffic": traffic}
+
+    copy = None
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            b.copy_(a)
+        c0.record()
+        for _ in range(10):
+            b.copy_(a)
+        c1.record()
+        torch.cuda.synchronize()
+        us = c0.elapsed_time(c1) * 100
+        copy = {"bytes_read": n, "bytes_written": n, "us_avg": round(us, 2),
+                "GBps": round(2 * n / us / 1e3, 1)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == synth.F32 else "bf16",
+        "data": "synthetic (seeded numpy PCG64 logits and gradients)",
+        "config": {"workload": f"{wl.name}: fused MoE router, T={T} tokens, E={E} experts, "
+                               f"K={K}, {sname}, step = " + " + ".join(kinds),
+                   "T": T, "E": E, "K": K, "score_function": sname,
+                   "logits": f"N(0, std {wl.logit_std})", "renorm": wl.renorm,
+                   "cache": "warm (one buffer set)" if args.warm else
+                            f"cold ({n_sets} rotating buffer sets, "
+                            f"{n_sets * set_bytes / 2**30:.2f} GiB)",
+                   "path_threshold": router.get_topk_path_threshold()},
+        "roofline": roof,
+        "kernels": kern,
+        "wall_s_timed_region": round(t_wall, 4),
+        "device": torch.cuda.get_device_name(0),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if copy:
+        out["copy_calibration"] = copy
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens or T)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,6 +51,12 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset outside every buffer
 
+// Cache policy of every row access: non-temporal (the gfx94x/gfx950 "nt"
+// bit).  Each byte is touched once, so streaming it past the caches keeps
+// them from thrashing; measured on MI355X it lifts the backward from ~5.3
+// to ~5.9 TB/s at E=2304.
+constexpr int kStream = 2;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     // 0x00020000: raw 32-bit data format word for the gfx9 family
@@ -62,49 +68,53 @@ template <typename TIn> struct io;
 
 template <> struct io<float> {
     static constexpr uint32_t kSize = 4;
+    template <int POL = kStream>
     __device__ static void load4(rsrc_t r, uint32_t off, uint32_t soff, float (&v)[4])
     {
-        auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0);
+        auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, POL);
         v[0] = as_f(t[0]); v[1] = as_f(t[1]); v[2] = as_f(t[2]); v[3] = as_f(t[3]);
     }
+    template <int POL = kStream>
     __device__ static float load1(rsrc_t r, uint32_t off)
     {
-        return as_f(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+        return as_f(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, POL));
     }
     __device__ static void store4(rsrc_t r, uint32_t off, const float (&v)[4])
     {
         __attribute__((ext_vector_type(4))) uint32_t t;
         t[0] = as_u(v[0]); t[1] = as_u(v[1]); t[2] = as_u(v[2]); t[3] = as_u(v[3]);
-        __builtin_amdgcn_raw_buffer_store_b128(t, r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(t, r, (int)off, 0, kStream);
     }
     __device__ static void store1(rsrc_t r, uint32_t off, float v)
     {
-        __builtin_amdgcn_raw_buffer_store_b32(as_u(v), r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(as_u(v), r, (int)off, 0, kStream);
     }
 };
 
 template <> struct io<uint16_t> {
     static constexpr uint32_t kSize = 2;
+    template <int POL = kStream>
     __device__ static void load4(rsrc_t r, uint32_t off, uint32_t soff, float (&v)[4])
     {
-        auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0);
+        auto t = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, POL);
         v[0] = as_f(t[0] << 16); v[1] = as_f(t[0] & 0xFFFF0000u);
         v[2] = as_f(t[1] << 16); v[3] = as_f(t[1] & 0xFFFF0000u);
     }
+    template <int POL = kStream>
     __device__ static float load1(rsrc_t r, uint32_t off)
     {
-        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, POL));
     }
     __device__ static void store4(rsrc_t r, uint32_t off, const float (&v)[4])
     {
         __attribute__((ext_vector_type(2))) uint32_t t;
         t[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
         t[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b64(t, r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(t, r, (int)off, 0, kStream);
     }
     __device__ static void store1(rsrc_t r, uint32_t off, float v)
     {
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, (int)off, 0, kStream);
     }
 };
 
@@ -119,15 +129,15 @@ __device__ __forceinline__ constexpr int jrel(int c, int u) { return c * 4 * LPT
 // Elements at or past Ev read as `pad`.  A masked access gets the VGPR
 // offset kOOB, which is out of range whether or not the hardware adds the
 // scalar offset to its range check, so it never touches memory.
-template <int LPT, typename T, bool VEC>
+template <int LPT, typename T, bool VEC, int POL = kStream>
 __device__ __forceinline__ void load_chunk(rsrc_t r, uint32_t goff, int c, int j_lane,
                                            int Ev, float pad, float (&v)[4])
 {
     const int j0 = jrel<LPT>(c, 0) + j_lane;
     if constexpr (VEC) {
         const bool ok = j0 < Ev;
-        io<T>::load4(r, ok ? (goff + (uint32_t)j_lane) * io<T>::kSize : kOOB,
-                     (uint32_t)jrel<LPT>(c, 0) * io<T>::kSize, v);
+        io<T>::template load4<POL>(r, ok ? (goff + (uint32_t)j_lane) * io<T>::kSize : kOOB,
+                                   (uint32_t)jrel<LPT>(c, 0) * io<T>::kSize, v);
 #pragma unroll
         for (int u = 0; u < 4; u++)
             v[u] = ok ? v[u] : pad;
@@ -135,7 +145,8 @@ __device__ __forceinline__ void load_chunk(rsrc_t r, uint32_t goff, int c, int j
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const bool ok = j0 + u < Ev;
-            const float t = io<T>::load1(r, ok ? (goff + (uint32_t)(j0 + u)) * io<T>::kSize : kOOB);
+            const float t = io<T>::template load1<POL>(
+                r, ok ? (goff + (uint32_t)(j0 + u)) * io<T>::kSize : kOOB);
             v[u] = ok ? t : pad;
         }
     }
@@ -165,14 +176,14 @@ __device__ __forceinline__ uint32_t load_map_chunk(rsrc_t r, uint32_t goff, int 
     if constexpr (VEC) {
         const bool ok = j0 < Ev;
         const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
-            r, (int)(ok ? goff + (uint32_t)j_lane : kOOB), jrel<LPT>(c, 0), 0);
+            r, (int)(ok ? goff + (uint32_t)j_lane : kOOB), jrel<LPT>(c, 0), kStream);
         return ok ? w : 0u;
     } else {
         uint32_t w = 0;
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const uint32_t b = __builtin_amdgcn_raw_buffer_load_b8(
-                r, (int)(j0 + u < Ev ? goff + (uint32_t)(j0 + u) : kOOB), 0, 0);
+                r, (int)(j0 + u < Ev ? goff + (uint32_t)(j0 + u) : kOOB), 0, kStream);
             w |= b << (8 * u);
         }
         return w;
@@ -186,13 +197,13 @@ __device__ __forceinline__ void store_map_chunk(rsrc_t r, uint32_t goff, int c, 
     const int j0 = jrel<LPT>(c, 0) + j_lane;
     if constexpr (VEC) {
         __builtin_amdgcn_raw_buffer_store_b32(w, r, (int)(j0 < E ? goff + (uint32_t)j0 : kOOB),
-                                              0, 0);
+                                              0, kStream);
     } else {
 #pragma unroll
         for (int u = 0; u < 4; u++)
             __builtin_amdgcn_raw_buffer_store_b8(
                 (uint8_t)(w >> (8 * u)), r,
-                (int)(j0 + u < E ? goff + (uint32_t)(j0 + u) : kOOB), 0, 0);
+                (int)(j0 + u < E ? goff + (uint32_t)(j0 + u) : kOOB), 0, kStream);
     }
 }
 
@@ -506,9 +517,9 @@ fwd_kernel(FwdParams p)
             for (int u = 0; u < 4; u++) {
                 key[c][u] = logit_key(x[c][u]);
                 if constexpr (SCORE == SCORE_SOFTMAX)
-                    s[c][u] = expf(x[c][u] - mx);              // padding: exp(-inf) = 0
+                    s[c][u] = exp_split(x[c][u] - mx);         // padding: exactly 0
                 else
-                    s[c][u] = 1.0f / (1.0f + expf(-x[c][u]));  // padding: 0
+                    s[c][u] = key[c][u] ? sigmoid_fast(x[c][u]) : 0.0f;
             }
         if constexpr (SCORE == SCORE_SOFTMAX) {
             const float z = group_sum<LPT>(tree_sum<VPL>(&s[0][0]));
@@ -533,7 +544,8 @@ fwd_kernel(FwdParams p)
 #pragma unroll
             for (int c = 0; c < NCH; c++) {
                 float b[4];
-                load_chunk<LPT, float, VEC>(rb, 0u, c, j_lane, Ev, 0.0f, b);
+                // the bias is shared by every token: default cache policy
+                load_chunk<LPT, float, VEC, 0>(rb, 0u, c, j_lane, Ev, 0.0f, b);
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const float r = s[c][u] + b[u];
@@ -570,8 +582,10 @@ fwd_kernel(FwdParams p)
                 uint32_t w = 0;
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
-                    const bool in = key[c][u] != 0u &&
-                                    pack_key(key[c][u], (uint32_t)(jrel<LPT>(c, u) + j_lane)) >= t64;
+                    // pack_key is 0 for excluded experts, and t64 > 0 on a real
+                    // token (idle groups store nothing)
+                    const bool in =
+                        pack_key(key[c][u], (uint32_t)(jrel<LPT>(c, u) + j_lane)) >= t64;
                     w |= (uint32_t)in << (8 * u);
                 }
                 mw[c] = w;

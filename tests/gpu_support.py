@@ -9,9 +9,10 @@ atol 1e-7, bf16 rtol 1e-2):
     keys s + b and group sums), both sides decide in fp32, but the GPU's
     fp32 score can differ from the correctly rounded one by an ulp; a token
     whose oracle margin between the last kept and the first dropped
-    candidate is below NEAR_TIE is a near-tie token: its map must be a
-    valid selection up to NEAR_TIE and its weights consistent with that
-    selection, and such tokens are counted;
+    candidate is below NEAR_TIE is a near-tie token; its map may differ from
+    the oracle's, but then it must be a valid selection up to NEAR_TIE with
+    weights consistent with that selection, and such rows are counted
+    (at most 1% of the tokens); every other map must match exactly;
   * values use |gpu - ref| <= atol + rtol |ref| (bf16: atol is 1e-2 times
     the row's largest |ref|).
 """
@@ -72,12 +73,50 @@ def tol_bad(gpu, ref, dtype, rtol=None, atol=None):
     return ~(np.abs(gpu - ref) <= lim)
 
 
-def assert_close(gpu, ref, dtype, what, rows=None, rtol=None, atol=None):
+def chain_tol(g, s, m, K, score_fn, renorm, c, aux=False, eps=F32_RTOL):
+    """Extra per-element tolerance of a chained backward (GPU forward then
+    GPU backward, against oracle forward then oracle backward): first-order
+    propagation of a relative error eps in every score s_j through
+    dx = alpha * base * (gm - beta) (the backward formulas of the router):
+    |d base| <= eps s, |d beta| <= eps sum|g| m s (softmax, no renorm) or
+    2 eps (sum|g| m s / A + |beta|) (renorm modes), |d alpha| <= eps |alpha|."""
+    g = np.asarray(g, np.float64)
+    s = np.asarray(s, np.float64)
+    m = np.ones_like(s) if aux else np.asarray(m, np.float64)
+    softmax = score_fn == synth.SOFTMAX
+    renorm_mode = renorm and ((not aux) if softmax else (aux or K > 1))
+    A = (m * s).sum(1, keepdims=True) if renorm_mode else np.ones((s.shape[0], 1))
+    B = (g * m * s).sum(1, keepdims=True)
+    G = (np.abs(g) * m * s).sum(1, keepdims=True)
+    cc = 1.0 if aux else c
+    base = s if softmax else s * (1 - s)
+    if renorm_mode:
+        alpha, beta = cc / A, B / A
+        e_beta = 2 * eps * (G / A + np.abs(beta))
+        e_alpha = eps * np.abs(alpha)
+        w = m
+        gm = g
+    else:
+        alpha = np.full_like(A, cc)
+        beta = B if softmax else np.zeros_like(B)
+        e_beta = eps * G if softmax else np.zeros_like(B)
+        e_alpha = np.zeros_like(A)
+        w = np.ones_like(s) if softmax else m
+        gm = g * m if softmax else g
+    d = np.abs(gm - beta)
+    return w * (np.abs(alpha) * eps * s * d + np.abs(alpha) * base * e_beta + e_alpha * base * d)
+
+
+def assert_close(gpu, ref, dtype, what, rows=None, rtol=None, atol=None, extra=None):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     if rows is not None:
         gpu, ref = gpu[rows], ref[rows]
+        extra = None if extra is None else extra[rows]
     bad = tol_bad(gpu, ref, dtype, rtol, atol)
+    if extra is not None:
+        bad &= np.abs(gpu - ref) > extra + (F32_ATOL if dtype == synth.F32 else 0.0) + \
+            (F32_RTOL if dtype == synth.F32 else BF16_RTOL) * np.abs(ref)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         worst = np.max(np.abs(gpu - ref))
@@ -154,16 +193,17 @@ def run_fwd(wl, T=None, check=True):
     assert_close(gi, S, synth.F32, f"{wl.name} intermediate")
     computed_keys = bias is not None or wl.num_groups > 0
     near = np.nonzero(margin < NEAR_TIE)[0] if computed_keys else np.zeros(0, int)
-    exact = np.setdiff1d(np.arange(x64.shape[0]), near)
-    diff = np.nonzero((gm[exact] != M[exact]).any(1))[0]
-    assert diff.size == 0, (f"{wl.name}: routing map differs on {diff.size} rows, "
-                            f"first {exact[diff[:5]].tolist()}")
-    assert_close(gp, P, wl.dtype, f"{wl.name} probs", rows=exact)
-    if near.size:
-        check_near_tie(near, gm, gp, S, x64, wl, bias)
-        assert near.size <= max(8, x64.shape[0] // 100), f"{near.size} near-tie rows"
+    differ = np.nonzero((gm != M).any(1))[0]
+    bad = np.setdiff1d(differ, near)
+    assert bad.size == 0, (f"{wl.name}: routing map differs on {bad.size} rows outside the "
+                           f"near-tie band, first {bad[:5].tolist()}")
+    same = np.setdiff1d(np.arange(x64.shape[0]), differ)
+    assert_close(gp, P, wl.dtype, f"{wl.name} probs", rows=same)
+    if differ.size:
+        check_near_tie(differ, gm, gp, S, x64, wl, bias)
+        assert differ.size <= max(8, x64.shape[0] // 100), f"{differ.size} rows differ"
     out["near"] = near
-    say(f"   ok; near-tie rows {near.size}")
+    say(f"   ok; near-tie rows {near.size}, of which maps differ on {differ.size}")
     return out
 
 

@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import (DEV, SCORE_NAME, assert_close, f64, run_aux_fwd, run_fwd, say,
-                         threads, to_dev)
+from gpu_support import (DEV, SCORE_NAME, assert_close, chain_tol, f64, run_aux_fwd, run_fwd,
+                         say, threads, to_dev)
 from score_function_top_amd import router, synth
 
 pytestmark = pytest.mark.gpu
@@ -85,8 +85,8 @@ def test_workload_backward_chained(name):
                           wl.scaling_factor, threads=threads())
     same = np.nonzero((f64(r["map"]) == r["M"]).all(1))[0]
     assert same.size >= wl.T - max(8, wl.T // 100)
-    assert_close(f64(dx), ref, wl.dtype, f"{name} chained grad", rows=same,
-                 rtol=1e-5 if wl.dtype == synth.F32 else None)
+    ext = chain_tol(g64, r["S"], r["M"], wl.K, wl.score_fn, wl.renorm, wl.scaling_factor)
+    assert_close(f64(dx), ref, wl.dtype, f"{name} chained grad", rows=same, extra=ext)
 
 
 @pytest.mark.parametrize("name", [n for n in WL if WL[n].aux])
@@ -105,7 +105,8 @@ def test_workload_aux(name):
                          threads=threads())
     assert_close(f64(dx), ref, wl.dtype, f"{name} aux grad")
     refc = oracle.aux_bwd(g64, r["S"], wl.score_fn, wl.aux_renorm, threads=threads())
-    assert_close(f64(dxc), refc, wl.dtype, f"{name} aux chained grad", rtol=1e-5)
+    ext = chain_tol(g64, r["S"], None, wl.K, wl.score_fn, wl.aux_renorm, 1.0, aux=True)
+    assert_close(f64(dxc), refc, wl.dtype, f"{name} aux chained grad", extra=ext)
 
 
 # ------------------------------------------------------------ E/K sweep
@@ -126,13 +127,15 @@ def test_sweep(E, K, sf):
     torch.cuda.synchronize()
     ref = oracle.topk_bwd(g64, r["S"], r["M"], K, sf, wl.renorm, wl.scaling_factor,
                           threads=threads())
-    assert_close(f64(dx), ref, wl.dtype, f"{wl.name} grad", rtol=1e-5)
+    ext = chain_tol(g64, r["S"], r["M"], K, sf, wl.renorm, wl.scaling_factor)
+    assert_close(f64(dx), ref, wl.dtype, f"{wl.name} grad", extra=ext)
     a = run_aux_fwd(wl, T=T)
     dxa = router.router_aux_scores_bwd(to_dev(g_st, wl.dtype), a["inter"], SCORE_NAME[sf],
                                        wl.aux_renorm)
     torch.cuda.synchronize()
     refa = oracle.aux_bwd(g64, a["S"], sf, wl.aux_renorm, threads=threads())
-    assert_close(f64(dxa), refa, wl.dtype, f"{wl.name} aux grad", rtol=1e-5)
+    ext = chain_tol(g64, a["S"], None, K, sf, wl.aux_renorm, 1.0, aux=True)
+    assert_close(f64(dxa), refa, wl.dtype, f"{wl.name} aux grad", extra=ext)
 
 
 # ------------------------------------------------------------ edge shapes
@@ -168,7 +171,8 @@ def test_edge_shapes(T, E, K, sf, renorm):
                                 SCORE_NAME[sf], renorm, 1.5)
     torch.cuda.synchronize()
     ref = oracle.topk_bwd(g64, r["S"], r["M"], K, sf, renorm, 1.5, threads=threads())
-    assert_close(f64(dx), ref, synth.F32, f"{wl.name} grad", rtol=1e-5)
+    ext = chain_tol(g64, r["S"], r["M"], K, sf, renorm, 1.5)
+    assert_close(f64(dx), ref, synth.F32, f"{wl.name} grad", extra=ext)
 
 
 @pytest.mark.parametrize("T,E,K,G,Kg,dtype", [
@@ -249,7 +253,7 @@ PATH_CASES = [(512, 2304, 36, synth.SOFTMAX, 0.0, 0), (700, 256, 4, synth.SOFTMA
 
 @pytest.mark.parametrize("T,E,K,sf,b,G", PATH_CASES)
 def test_path_parity(T, E, K, sf, b, G):
-    """Every selection path gives the same map and bit-identical weights."""
+    """Every selection path gives the same map and the same weights."""
     wl = edge_wl(T, E, K, sf, True, bias=b, G=G, Kg=4 if G else 0, c=2.0, seed=23)
     outs = []
     try:
@@ -259,9 +263,12 @@ def test_path_parity(T, E, K, sf, b, G):
             outs.append((f64(r["probs"]), f64(r["map"]), f64(r["inter"])))
     finally:
         router.set_topk_path_threshold(8)
+    # maps are identical; weights may differ in the last bits where the
+    # paths use different lane-group widths (different reduction trees)
     for o in outs[1:]:
         assert (o[1] == outs[0][1]).all(), "maps differ between paths"
-        assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[2], outs[0][2])
+        assert_close(o[0], outs[0][0], synth.F32, "probs across paths", rtol=1e-6, atol=0)
+        assert_close(o[2], outs[0][2], synth.F32, "intermediate across paths", rtol=1e-6, atol=0)
 
 
 def test_deterministic():
@@ -307,7 +314,8 @@ def test_unaligned_views(E, K, sf):
     assert_close(f64(p), P, synth.F32, "unaligned probs")
     assert_close(f64(i), S, synth.F32, "unaligned intermediate")
     ref = oracle.topk_bwd(g64, S, M, K, sf, wl.renorm, 1.25, threads=threads())
-    assert_close(f64(dx), ref, synth.F32, "unaligned grad", rtol=1e-5)
+    ext = chain_tol(g64, S, M, K, sf, wl.renorm, 1.25)
+    assert_close(f64(dx), ref, synth.F32, "unaligned grad", extra=ext)
 
 
 def test_zero_tokens():
@@ -355,5 +363,6 @@ def test_beyond_32bit_elements():
     del x
     dx = router.router_topk_bwd(g, i, m, K, "sigmoid", True, 2.0)
     torch.cuda.synchronize()
-    ref = oracle.topk_bwd(f64(g[rt]), f64(i[rt]), f64(m[rt]), K, synth.SIGMOID, True, 2.0)
-    assert_close(f64(dx[rt]), ref, synth.F32, "large grad")
+    ref = oracle.topk_bwd(f64(g[rt]), S, M, K, synth.SIGMOID, True, 2.0)
+    ext = chain_tol(f64(g[rt]), S, M, K, synth.SIGMOID, True, 2.0)
+    assert_close(f64(dx[rt]), ref, synth.F32, "large grad", extra=ext)

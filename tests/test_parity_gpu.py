@@ -366,3 +366,51 @@ def test_beyond_32bit_elements():
     ref = oracle.topk_bwd(f64(g[rt]), S, M, K, synth.SIGMOID, True, 2.0)
     ext = chain_tol(f64(g[rt]), S, M, K, synth.SIGMOID, True, 2.0)
     assert_close(f64(dx[rt]), ref, synth.F32, "large grad", extra=ext)
+
+
+def test_graph_replay_matches_eager():
+    """The four passes captured in one HIP graph: every replay, with eager
+    work and synchronisation between replays, equals the eager results bit
+    for bit (no memset nodes: the library writes every output element)."""
+    wl = WL["c3_sigmoid_512x22"]
+    x_st, _ = wl.logits()
+    g_st, _ = wl.grad()
+    T = 2048
+    x = to_dev(x_st[:T], wl.dtype)
+    g = to_dev(g_st[:T], wl.dtype)
+    b = torch.from_numpy(wl.bias()).to(DEV)
+    say("[graph] c3 slice")
+
+    def passes(o):
+        router.router_topk_fwd(x, wl.K, "sigmoid", True, 0, 0, 2.5, b,
+                               out=(o["p"], o["m"], o["i"]))
+        router.router_topk_bwd(g, o["i"], o["m"], wl.K, "sigmoid", True, 2.5, out=o["dx"])
+        router.router_aux_scores(x, wl.K, "sigmoid", True, out=(o["a"], o["am"], o["ai"]))
+        router.router_aux_scores_bwd(g, o["ai"], "sigmoid", True, out=o["adx"])
+
+    def bufs():
+        o = {k: torch.empty(T, wl.E, device=DEV) for k in ("p", "i", "dx", "a", "ai", "adx")}
+        o.update({k: torch.empty(T, wl.E, dtype=torch.bool, device=DEV) for k in ("m", "am")})
+        return o
+
+    eager, cap = bufs(), bufs()
+    passes(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        passes(cap)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        passes(cap)
+    other = bufs()
+    for rep in range(3):
+        for t in cap.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        passes(other)                 # eager work between replays
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(cap[k], eager[k]), (rep, k)
+            assert torch.equal(other[k], eager[k]), (rep, k)

@@ -34,11 +34,12 @@ enum : int {
     kRowBcast31 = 0x143,  // lane 31 feeds rows 2 and 3
 };
 
+// Lane permutation inside 16-lane rows; every source lane is valid for the
+// controls used here, so no "old" value is needed.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)v, CTRL, 0xF,
-                                                 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
 // Value held by lane (lane ^ J) of the same group; J < LPT.
@@ -240,16 +241,17 @@ __device__ __forceinline__ uint64_t partner_mirror64(uint64_t v)
     return ((uint64_t)h << 32) | l;
 }
 
+// Compare-exchange: the lower lane of a pair keeps the larger value, the
+// upper lane the smaller; i.e. take the partner's value when it is larger
+// exactly on the lower lane.
 __device__ __forceinline__ uint64_t keep(uint64_t mine, uint64_t other, bool lower)
 {
-    uint64_t hi = mine > other ? mine : other;
-    uint64_t lo = mine > other ? other : mine;
-    return lower ? hi : lo;
+    return ((other > mine) == lower) ? other : mine;
 }
 
 __device__ __forceinline__ uint32_t keep32(uint32_t mine, uint32_t other, bool lower)
 {
-    return lower ? (mine > other ? mine : other) : (mine > other ? other : mine);
+    return ((other > mine) == lower) ? other : mine;
 }
 
 template <int J>

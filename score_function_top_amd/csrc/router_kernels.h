@@ -219,86 +219,99 @@ __device__ __forceinline__ float tree_sum(const float *v)
     }
 }
 
-__device__ __forceinline__ uint64_t pack_key(uint32_t key, uint32_t j)
-{
-    return key ? (((uint64_t)key << 32) | (uint32_t)~j) : 0ull;
-}
-
-// Key of a logit: 0 for padding (-inf), else the order-preserving key of
-// x + 0.0 (so that -0.0 and +0.0, equal logits, tie).
-__device__ __forceinline__ uint32_t logit_key(float x)
-{
-    return x == -INFINITY ? 0u : ord_key(x + 0.0f);
-}
-
 // ------------------------------------------------------------ selection
+//
+// Selection keys are floats: the logit without a bias, fp32(s + b) with
+// one; -inf marks padding and experts outside the kept groups (finite
+// logits are a precondition).  Equal keys tie (-0.0 == +0.0) and ties go to
+// the lower index.  A selection is described by its threshold (x, j):
+// expert j with key k is selected iff k > x, or k == x and j <= j_t.
+// Where a total order is needed (sorting, group-wide maxima) a key is packed
+// as ord(k) << 32 | ~j: ord is monotone and canonical on +-0, and ~j makes
+// the lower index the larger pack.
 
-// Marks a selected expert during argmax rounds: below every real key
-// (>= 0x00800000) and above the "no candidate" 0.
-constexpr uint32_t kTaken = 1u;
+struct Thresh {
+    float x;
+    uint32_t j;   // 0xFFFFFFFF: every key equal to x is selected
+};
 
-// argmax: K rounds; each round the group's largest pack value wins and its
-// key becomes kTaken.  Afterwards the selected experts are the kTaken keys.
+__device__ __forceinline__ uint64_t pack_key(float k, uint32_t j)
+{
+    return ((uint64_t)ord_key(k + 0.0f) << 32) | (uint32_t)~j;
+}
+
+__device__ __forceinline__ Thresh unpack_thresh(uint64_t t64)
+{
+    return Thresh{ord_key_inv((uint32_t)(t64 >> 32)), ~(uint32_t)t64};
+}
+
+// Largest finite float: the lowest threshold a real key can need.
+constexpr float kMinKey = -3.4028234663852886e38f;
+
+// argmax: K rounds; each round the group's largest (key, lower index) wins
+// and its key becomes NaN (never compares larger again).  Afterwards the
+// selected experts are exactly the NaN keys.
 template <int LPT, int NCH>
-__device__ __forceinline__ void select_argmax(uint32_t (&key)[NCH][4], int K, int j_lane)
+__device__ __forceinline__ void select_argmax(float (&key)[NCH][4], int K, int j_lane)
 {
     for (int r = 0; r < K; r++) {
         // lane-local best: first (lowest j) element with the largest key
-        uint32_t bk = key[0][0];
+        float bk = -INFINITY;
         uint32_t bj = 0;
 #pragma unroll
         for (int c = 0; c < NCH; c++)
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                if (c == 0 && u == 0)
-                    continue;
                 const bool gt = key[c][u] > bk;
                 bk = gt ? key[c][u] : bk;
                 bj = gt ? (uint32_t)jrel<LPT>(c, u) : bj;
             }
-        const uint64_t best =
-            group_max_u64<LPT>(pack_key(bk > kTaken ? bk : 0u, bj + (uint32_t)j_lane));
+        const uint64_t mine = bk == -INFINITY ? 0ull : pack_key(bk, bj + (uint32_t)j_lane);
+        const uint64_t best = group_max_u64<LPT>(mine);
         // winner's j relative to this lane; no match when there is no winner
         const uint32_t jw = best ? ~(uint32_t)best - (uint32_t)j_lane : 0xFFFFFFFFu;
 #pragma unroll
         for (int c = 0; c < NCH; c++)
 #pragma unroll
             for (int u = 0; u < 4; u++)
-                key[c][u] = jw == (uint32_t)jrel<LPT>(c, u) ? kTaken : key[c][u];
+                key[c][u] = jw == (uint32_t)jrel<LPT>(c, u) ? __builtin_nanf("") : key[c][u];
     }
 }
 
-// bits: exact search, any K.  Finds the K-th largest key value v, then
-// among keys equal to v the index of the (K - #{key > v})-th lowest.
+// bits: exact search, any K.  Finds the K-th largest key value v by a
+// bit-by-bit search over its order-preserving u32 code (each candidate code
+// is mapped back to a float and compared), then, if more keys equal v than
+// the selection needs, the index of the last selected one.
 template <int LPT, int NCH>
-__device__ __forceinline__ uint64_t select_bits(const uint32_t (&key)[NCH][4],
-                                                int K, int j_lane)
+__device__ __forceinline__ Thresh select_bits(const float (&key)[NCH][4], int K, int j_lane)
 {
     uint32_t pref = 0;
     for (int b = 31; b >= 0; b--) {
         const uint32_t cand = pref | (1u << b);
+        const float cf = ord_key_inv(cand);  // NaN codes count nothing
         uint32_t cnt = 0;
 #pragma unroll
         for (int c = 0; c < NCH; c++)
 #pragma unroll
             for (int u = 0; u < 4; u++)
-                cnt += key[c][u] >= cand;
+                cnt += key[c][u] >= cf;
         pref = group_sum_u32<LPT>(cnt) >= (uint32_t)K ? cand : pref;
     }
+    const float v = ord_key_inv(pref);
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int c = 0; c < NCH; c++)
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            gt += key[c][u] > pref;
-            eq += key[c][u] == pref;
+            gt += key[c][u] > v;
+            eq += key[c][u] == v;
         }
     gt = group_sum_u32<LPT>(gt);
     eq = group_sum_u32<LPT>(eq);
     const uint32_t need = (uint32_t)K - gt;
-    uint32_t J = 0xFFFFFFFFu;  // every key equal to pref is selected
+    uint32_t J = 0xFFFFFFFFu;
     if (wave_any(eq != need)) {
-        // lowest J with #{key == pref, j <= J} >= need
+        // lowest J with #{key == v, j <= J} >= need
         uint32_t lo = 0;
         for (int b = 31 - __builtin_clz(NCH * 4 * LPT); b >= 0; b--) {
             const int test = (int)(lo + (1u << b) - 1u) - j_lane;  // lane-relative
@@ -307,32 +320,34 @@ __device__ __forceinline__ uint64_t select_bits(const uint32_t (&key)[NCH][4],
             for (int c = 0; c < NCH; c++)
 #pragma unroll
                 for (int u = 0; u < 4; u++)
-                    f += (key[c][u] == pref) & (jrel<LPT>(c, u) <= test);
+                    f += (key[c][u] == v) & (jrel<LPT>(c, u) <= test);
             lo = group_sum_u32<LPT>(f) < need ? lo + (1u << b) : lo;
         }
         J = eq != need ? lo : J;
     }
-    return ((uint64_t)pref << 32) | (uint32_t)~J;
+    return Thresh{v, J};
 }
 
-// prune: candidates >= tau (the K-th largest lane maximum) compacted into
-// this group's LDS list, sorted, K-th taken.  The list has 2*LPT slots plus
-// one dummy slot per lane that absorbs the writes of non-candidates.  Falls
-// back to select_bits for the whole wave when a group has more than 2*LPT
+// prune: keys >= tau (the K-th largest lane maximum; K lanes hold a key >=
+// tau, so the K-th largest key is >= tau) are compacted into this group's
+// LDS list -- raw key bits and ~j, 2*LPT slots plus one dummy slot per lane
+// for the writes of non-candidates -- read back at most two per lane,
+// packed, bitonic-sorted, and the K-th taken.  When the (K+1)-th has a
+// different key, no tie straddles the threshold and j_t is "all".  Falls back
+// to select_bits for the whole wave when a group has more than 2*LPT
 // candidates.  Requires K <= LPT.
 template <int LPT, int NCH>
-__device__ __forceinline__ uint64_t select_prune(const uint32_t (&key)[NCH][4],
-                                                 int K, int lane, int j_lane,
-                                                 uint64_t *cand)
+__device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K, int lane,
+                                               int j_lane, uint64_t *cand)
 {
-    uint32_t lm = 0;
+    float lm = -INFINITY;
 #pragma unroll
     for (int c = 0; c < NCH; c++)
 #pragma unroll
         for (int u = 0; u < 4; u++)
-            lm = key[c][u] > lm ? key[c][u] : lm;
-    uint32_t tau = group_bcast<LPT>(sort_desc32<LPT>(lm), K - 1);
-    tau = tau ? tau : 1u;  // padding and excluded experts never compete
+            lm = fmaxf(lm, key[c][u]);
+    float tau = ord_key_inv(group_bcast<LPT>(sort_desc32<LPT>(ord_key(lm + 0.0f)), K - 1));
+    tau = fmaxf(tau, kMinKey);  // padding and excluded experts never compete
     uint32_t cnt = 0;
 #pragma unroll
     for (int c = 0; c < NCH; c++)
@@ -349,31 +364,44 @@ __device__ __forceinline__ uint64_t select_prune(const uint32_t (&key)[NCH][4],
     for (int c = 0; c < NCH; c++)
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            const bool in = key[c][u] >= tau;
-            cand[in ? pos : dummy] = pack_key(key[c][u], (uint32_t)(jrel<LPT>(c, u) + j_lane));
+            // same test as the count, spelled so the compiler recomputes it
+            // instead of keeping 36 lane masks alive (keys are never NaN here)
+            const bool in = !(key[c][u] < tau);
+            cand[in ? pos : dummy] = ((uint64_t)as_u(key[c][u]) << 32) |
+                                     (uint32_t)~(uint32_t)(jrel<LPT>(c, u) + j_lane);
             pos += in;
         }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    auto repack = [](uint64_t raw) {
+        return ((uint64_t)ord_key(as_f((uint32_t)(raw >> 32)) + 0.0f) << 32) | (uint32_t)raw;
+    };
     uint64_t v0 = cand[lane];
-    v0 = (uint32_t)lane < total ? v0 : 0ull;
+    v0 = (uint32_t)lane < total ? repack(v0) : 0ull;
+    uint64_t next;
     if (wave_any(total > (uint32_t)LPT)) {
         uint64_t v1 = cand[lane + LPT];
-        v1 = (uint32_t)(lane + LPT) < total ? v1 : 0ull;
+        v1 = (uint32_t)(lane + LPT) < total ? repack(v1) : 0ull;
         sort_desc64x2<LPT>(v0, v1);
+        // the (K+1)-th: position K, in the second half when K == LPT
+        next = K < LPT ? group_bcast64<LPT>(v0, K) : group_bcast64<LPT>(v1, 0);
     } else {
         v0 = sort_desc64<LPT>(v0);
+        next = K < LPT ? group_bcast64<LPT>(v0, K) : 0ull;
     }
     const uint64_t t64 = group_bcast64<LPT>(v0, K - 1);  // K <= LPT: in the first half
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    return t64;
+    Thresh t = unpack_thresh(t64);
+    if ((next >> 32) != (t64 >> 32))
+        t.j = 0xFFFFFFFFu;
+    return t;
 }
 
 // Group-limited routing.  Group g = experts [g*P, (g+1)*P); its score is
 // the fp32 sum of its q largest values s + b, largest first; the Kg best
 // groups stay (ties keep the lower group) and the keys of every other
-// expert are cleared.  The caller first stores each element's value with
+// expert become -inf.  The caller first stores each element's value with
 // group_value_store into gscr (group_scratch_floats(E, G, LPT) floats of
 // LDS for this token group: one padding word after each group so the
 // per-group scans touch distinct banks, and a dummy word per lane for
@@ -391,7 +419,7 @@ __device__ __forceinline__ void group_value_store(float *gscr, int j, bool real,
 }
 
 template <int LPT, int NCH>
-__device__ __forceinline__ void group_limit(uint32_t (&key)[NCH][4], const FwdParams &p,
+__device__ __forceinline__ void group_limit(float (&key)[NCH][4], const FwdParams &p,
                                             int lane, int j_lane, bool tok, float invP,
                                             const float *gscr)
 {
@@ -449,7 +477,7 @@ __device__ __forceinline__ void group_limit(uint32_t (&key)[NCH][4], const FwdPa
         for (int u = 0; u < 4; u++) {
             const int g = group_of(jrel<LPT>(c, u) + j_lane, invP);
             const bool in = g < G && ((gmask >> (g & 63)) & 1ull);
-            key[c][u] = in ? key[c][u] : 0u;
+            key[c][u] = in ? key[c][u] : -INFINITY;
         }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -491,14 +519,14 @@ fwd_kernel(FwdParams p)
         const uint32_t nel = (uint32_t)(nval * E);
         const rsrc_t rx = make_rsrc(static_cast<const TIn *>(p.x) + off0, nel * io<TIn>::kSize);
 
-        float x[NCH][4];
+        // key[][] holds the logits (-inf on padding) and becomes the keys
+        float key[NCH][4];
 #pragma unroll
         for (int c = 0; c < NCH; c++)
-            load_chunk<LPT, TIn, VEC>(rx, goff, c, j_lane, Ev, -INFINITY, x[c]);
+            load_chunk<LPT, TIn, VEC>(rx, goff, c, j_lane, Ev, -INFINITY, key[c]);
         __builtin_amdgcn_sched_barrier(0);  // every load in flight before any math
 
-        // ---- score function; logit keys (0 on padding)
-        uint32_t key[NCH][4];
+        // ---- score function
         float s[NCH][4];
         float mx = 0.0f;
         if constexpr (SCORE == SCORE_SOFTMAX) {
@@ -507,7 +535,7 @@ fwd_kernel(FwdParams p)
             for (int c = 0; c < NCH; c++)
 #pragma unroll
                 for (int u = 0; u < 4; u++)
-                    m = fmaxf(m, x[c][u]);
+                    m = fmaxf(m, key[c][u]);
             mx = group_max<LPT>(m);
             mx = tok ? mx : 0.0f;
         }
@@ -515,11 +543,10 @@ fwd_kernel(FwdParams p)
         for (int c = 0; c < NCH; c++)
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                key[c][u] = logit_key(x[c][u]);
                 if constexpr (SCORE == SCORE_SOFTMAX)
-                    s[c][u] = exp_split(x[c][u] - mx);         // padding: exactly 0
+                    s[c][u] = exp_split(key[c][u] - mx);           // padding: exactly 0
                 else
-                    s[c][u] = key[c][u] ? sigmoid_fast(x[c][u]) : 0.0f;
+                    s[c][u] = key[c][u] == -INFINITY ? 0.0f : sigmoid_fast(key[c][u]);
             }
         if constexpr (SCORE == SCORE_SOFTMAX) {
             const float z = group_sum<LPT>(tree_sum<VPL>(&s[0][0]));
@@ -549,11 +576,11 @@ fwd_kernel(FwdParams p)
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const float r = s[c][u] + b[u];
-                    const bool real = key[c][u] != 0u;
+                    const bool real = key[c][u] != -INFINITY;
                     if constexpr (GROUPED)
                         group_value_store(gscr, jrel<LPT>(c, u) + j_lane, real, r, p, invP, lane);
                     if (has_bias)
-                        key[c][u] = real ? ord_key(r + 0.0f) : 0u;
+                        key[c][u] = real ? r : -INFINITY;
                 }
             }
         }
@@ -570,25 +597,38 @@ fwd_kernel(FwdParams p)
                 uint32_t w = 0;
 #pragma unroll
                 for (int u = 0; u < 4; u++)
-                    w |= (uint32_t)(key[c][u] == kTaken) << (8 * u);
+                    w |= (uint32_t)(key[c][u] != key[c][u]) << (8 * u);  // NaN: taken
                 mw[c] = w;
             }
         } else {
-            const uint64_t t64 = p.sel == SEL_BITS
-                                     ? select_bits<LPT, NCH>(key, p.K, j_lane)
-                                     : select_prune<LPT, NCH>(key, p.K, lane, j_lane, cand);
+            const Thresh t = p.sel == SEL_BITS
+                                 ? select_bits<LPT, NCH>(key, p.K, j_lane)
+                                 : select_prune<LPT, NCH>(key, p.K, lane, j_lane, cand);
+            // idle groups (past T) store nothing; give them a threshold no key meets
+            const float tx = tok ? t.x : INFINITY;
+            if (!wave_any(t.j != 0xFFFFFFFFu)) {
 #pragma unroll
-            for (int c = 0; c < NCH; c++) {
-                uint32_t w = 0;
+                for (int c = 0; c < NCH; c++) {
+                    uint32_t w = 0;
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    // pack_key is 0 for excluded experts, and t64 > 0 on a real
-                    // token (idle groups store nothing)
-                    const bool in =
-                        pack_key(key[c][u], (uint32_t)(jrel<LPT>(c, u) + j_lane)) >= t64;
-                    w |= (uint32_t)in << (8 * u);
+                    for (int u = 0; u < 4; u++)
+                        w |= (uint32_t)(key[c][u] >= tx) << (8 * u);
+                    mw[c] = w;
                 }
-                mw[c] = w;
+            } else {
+                const int jt = (int)t.j - j_lane;  // lane-relative; "all" stays large
+#pragma unroll
+                for (int c = 0; c < NCH; c++) {
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        const float k = key[c][u];
+                        const bool in = k > tx || (k == tx && (t.j == 0xFFFFFFFFu ||
+                                                               jrel<LPT>(c, u) <= jt));
+                        w |= (uint32_t)in << (8 * u);
+                    }
+                    mw[c] = w;
+                }
             }
         }
 

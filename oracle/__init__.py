@@ -1,5 +1,6 @@
 """fp64 CPU oracle of the fused MoE router (score function + top-k, its
-backward, and the aux-loss score variant).
+backward, the aux-loss score variant, and the load-balancing loss over the
+aux scores).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code
@@ -50,8 +51,14 @@ def _load(path=None):
                                     ctypes.c_double, d]
     lib.oracle_aux_fwd.argtypes = [d, i64, i32, i32, i32, i32, d, u8, d]
     lib.oracle_aux_bwd.argtypes = [d, d, i64, i32, i32, i32, d]
+    q = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_tokens_per_expert.argtypes = [u8, i64, i32, q]
+    lib.oracle_aux_loss.argtypes = [d, q, i64, i32, i64, i32, ctypes.c_double, d]
+    lib.oracle_aux_loss_bwd.argtypes = [ctypes.c_double, q, i64, i32, i64, i32,
+                                        ctypes.c_double, d]
     for f in (lib.oracle_topk_fwd, lib.oracle_topk_bwd, lib.oracle_aux_fwd,
-              lib.oracle_aux_bwd):
+              lib.oracle_aux_bwd, lib.oracle_tokens_per_expert, lib.oracle_aux_loss,
+              lib.oracle_aux_loss_bwd):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -190,3 +197,42 @@ def aux_bwd(g, s, score_fn=SOFTMAX, renorm=True, threads=1, lib=None):
     if err:
         raise OracleError("oracle_aux_bwd rejected its arguments")
     return dx
+
+
+def tokens_per_expert(rmap, lib=None):
+    """Column counts of a routing map [T,E] -> int64 [E]."""
+    lib = lib or _load()
+    m = np.ascontiguousarray(rmap, dtype=np.uint8)
+    T, E = m.shape
+    out = np.empty((E,), np.int64)
+    if lib.oracle_tokens_per_expert(_p(m, ctypes.c_uint8), T, E,
+                                    _p(out, ctypes.c_int64)) != 0:
+        raise OracleError("oracle_tokens_per_expert rejected its arguments")
+    return out
+
+
+def aux_loss(scores, counts, K, coeff, total_tokens=None, lib=None):
+    """Load-balancing loss (float) of scores [T,E] and counts [E]."""
+    lib = lib or _load()
+    s = _f64(scores)
+    c = np.ascontiguousarray(counts, dtype=np.int64)
+    T, E = s.shape
+    N = T if total_tokens is None else int(total_tokens)
+    out = ctypes.c_double()
+    if lib.oracle_aux_loss(_p(s, ctypes.c_double), _p(c, ctypes.c_int64), T, E, N, K,
+                           float(coeff), ctypes.byref(out)) != 0:
+        raise OracleError("oracle_aux_loss rejected its arguments")
+    return out.value
+
+
+def aux_loss_bwd(grad_loss, counts, T, K, coeff, total_tokens=None, lib=None):
+    """Gradient [T,E] of the loss with respect to the scores."""
+    lib = lib or _load()
+    c = np.ascontiguousarray(counts, dtype=np.int64)
+    E = c.shape[0]
+    N = T if total_tokens is None else int(total_tokens)
+    out = np.empty((T, E), np.float64)
+    if lib.oracle_aux_loss_bwd(float(grad_loss), _p(c, ctypes.c_int64), T, E, N, K,
+                               float(coeff), _p(out, ctypes.c_double)) != 0:
+        raise OracleError("oracle_aux_loss_bwd rejected its arguments")
+    return out

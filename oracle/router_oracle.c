@@ -18,13 +18,18 @@
  *     pass 2 writes one gradient per element.
  *   - greptile "Confidence Score": several score functions, each with and
  *     without pre-softmax.
+ *   - "Files changed", fused_moe_aux_loss.cu: the load-balancing loss that
+ *     consumes the aux scores (the page names the kernel, not its formula).
  * The pages give no formula.  Readings used where they are silent:
  *   softmax = exp(x - max) / sum; sigmoid = 1 / (1 + exp(-x)); expert bias
  *   and groups influence selection only; group score = sum of the q = K/Kg
  *   largest biased scores of the group; ties go to the lower index (expert
  *   or group); renormalisation divides by the sum of the selected scores
  *   (skipped for sigmoid with K == 1); the scaling factor multiplies last;
- *   intermediate = the full-row score for every mode.
+ *   intermediate = the full-row score for every mode; the aux loss is the
+ *   Switch-Transformer balancing loss extended to top-K,
+ *   coeff * E / (N^2 K) * sum_i n_i * sum_t scores[t,i], n_i the tokens
+ *   routed to expert i, N the tokens those counts cover.
  *
  * Precision: every value is fp64, except where floating point decides an
  * integer.  With an expert bias the selection key is r = s + b evaluated in
@@ -362,5 +367,76 @@ int oracle_aux_bwd(const double *g, const double *s, int64_t T, int E,
                 dr[i] = gr[i] * sr[i] * (1.0 - sr[i]);
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------- aux loss scalar */
+
+/*
+ * Tokens routed to each expert: counts[i] = sum over tokens of map[t,i].
+ */
+int oracle_tokens_per_expert(const uint8_t *map, int64_t T, int E,
+                             int64_t *counts)
+{
+    int64_t t;
+    int i;
+
+    if (T < 0 || E < 1)
+        return -1;
+    for (i = 0; i < E; i++)
+        counts[i] = 0;
+    for (t = 0; t < T; t++)
+        for (i = 0; i < E; i++)
+            counts[i] += map[t * E + i] ? 1 : 0;
+    return 0;
+}
+
+/*
+ * Load-balancing loss over the aux scores (the router page names the
+ * fused_moe_aux_loss kernel but not its formula; reading: the Switch
+ * Transformer balancing loss extended to top-K routing):
+ *   L = coeff * E / (N^2 K) * sum_i counts[i] * sum_t scores[t,i]
+ * i.e. coeff * E * sum_i f_i P_i with f_i = counts[i] / (N K) and
+ * P_i = sum_t scores[t,i] / N.  N = total_tokens (the tokens the counts and
+ * the normalisation refer to).  *loss receives L.
+ */
+int oracle_aux_loss(const double *scores, const int64_t *counts, int64_t T,
+                    int E, int64_t N, int K, double coeff, double *loss)
+{
+    int64_t t;
+    int i;
+    double acc = 0.0;
+
+    if (T < 0 || E < 1 || N < 1 || K < 1)
+        return -1;
+    for (i = 0; i < E; i++) {
+        double col = 0.0;
+        for (t = 0; t < T; t++)
+            col += scores[t * E + i];
+        acc += (double)counts[i] * col;
+    }
+    *loss = coeff * (double)E / ((double)N * (double)N * (double)K) * acc;
+    return 0;
+}
+
+/*
+ * Gradient of the loss above with respect to the scores, times grad_loss:
+ *   grad_scores[t,i] = grad_loss * coeff * E * counts[i] / (N^2 K)
+ * (the counts are integers and carry no gradient).
+ */
+int oracle_aux_loss_bwd(double grad_loss, const int64_t *counts, int64_t T,
+                        int E, int64_t N, int K, double coeff,
+                        double *grad_scores)
+{
+    int64_t t;
+    int i;
+
+    if (T < 0 || E < 1 || N < 1 || K < 1)
+        return -1;
+    for (t = 0; t < T; t++)
+        for (i = 0; i < E; i++)
+            grad_scores[t * E + i] = grad_loss * coeff * (double)E *
+                                     (double)counts[i] /
+                                     ((double)N * (double)N * (double)K);
     return 0;
 }

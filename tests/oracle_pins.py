@@ -116,7 +116,7 @@ def parse_golden(path):
                 vals = [float(Fraction(t)) for t in v.split()]
                 cur[k] = vals if len(vals) > 1 or k in (
                     "w", "s", "m", "g", "map", "probs", "inter", "scores",
-                    "dx", "bias") else vals[0]
+                    "dx", "bias", "counts", "dscore") else vals[0]
     return cases
 
 
@@ -130,6 +130,10 @@ def pin_golden(lib):
             continue
         for c in parse_golden(os.path.join(GOLDEN, fn)):
             what = f"{fn}:{c['case']}"
+            if c["op"] == "aux_loss":
+                golden_aux_loss(lib, c, what)
+                n += 1
+                continue
             sf = SCORE[c["score"]]
             if c["op"] == "topk_fwd":
                 x = np.log(np.array(c["w"]))[None]
@@ -162,7 +166,21 @@ def pin_golden(lib):
             else:
                 raise AssertionError(what)
             n += 1
-    assert n == 18, n
+    assert n == 21, n
+
+
+def golden_aux_loss(lib, c, what):
+    E = int(c["E"])
+    sc = np.array(c["scores"]).reshape(-1, E)
+    if "map" in c:
+        m = np.array(c["map"], np.uint8).reshape(-1, E)
+        cnt = oracle.tokens_per_expert(m, lib=lib)
+        assert (cnt == np.array(c["counts"])).all(), (what, cnt)
+    cnt = np.array(c["counts"], np.int64)
+    K, coeff, N = int(c["K"]), c["coeff"], int(c["N"])
+    close(oracle.aux_loss(sc, cnt, K, coeff, N, lib=lib), c["loss"], what=what + " loss")
+    d = oracle.aux_loss_bwd(c["grad_loss"], cnt, sc.shape[0], K, coeff, N, lib=lib)
+    close(d.ravel(), c["dscore"], what=what + " dscore")
 
 
 def pin_score_library(lib):
@@ -401,7 +419,71 @@ def pin_margin(lib):
     assert np.isinf(mg[0])
 
 
+def pin_tokens_per_expert(lib):
+    """Column counts of random maps equal numpy's column sums, including a
+    map with empty columns and one with no rows."""
+    rng = np.random.default_rng(11)
+    for T, E, p in ((1, 1, 0.5), (7, 5, 0.3), (33, 64, 0.05), (64, 9, 0.9)):
+        m = (rng.random((T, E)) < p).astype(np.uint8)
+        m[:, 0] = 0
+        assert (oracle.tokens_per_expert(m, lib=lib) == m.sum(0)).all(), (T, E)
+    assert (oracle.tokens_per_expert(np.zeros((0, 6), np.uint8), lib=lib) == 0).all()
+
+
+def pin_aux_loss_closed_forms(lib):
+    """Balanced routing (every score 1/E, every count N K / E) gives exactly
+    coeff; one expert taking everything gives coeff * E; the loss is linear
+    in the scores, scales as 1/N^2 at fixed sums, and is invariant to the
+    order of the tokens and to a relabelling of the experts."""
+    rng = np.random.default_rng(12)
+    for N, E, K, coeff in ((8, 4, 2, 0.01), (12, 6, 3, 1.0), (64, 16, 4, 1e-3)):
+        sc = np.full((N, E), 1.0 / E)
+        cnt = np.full(E, N * K // E, np.int64)
+        close(oracle.aux_loss(sc, cnt, K, coeff, lib=lib), coeff, what="balanced")
+        sc = np.zeros((N, E))
+        sc[:, 1] = 1.0
+        cnt = np.zeros(E, np.int64)
+        cnt[1] = N * K
+        close(oracle.aux_loss(sc, cnt, K, coeff, lib=lib), coeff * E,
+              what="collapse")
+    T, E, K = 9, 7, 3
+    a, b = rng.random((T, E)), rng.random((T, E))
+    cnt = rng.integers(0, 20, E)
+    la = oracle.aux_loss(a, cnt, K, 0.3, 40, lib=lib)
+    lb = oracle.aux_loss(b, cnt, K, 0.3, 40, lib=lib)
+    close(oracle.aux_loss(2 * a - b, cnt, K, 0.3, 40, lib=lib), 2 * la - lb, what="linear")
+    close(oracle.aux_loss(a, cnt, K, 0.3, 80, lib=lib), la / 4, what="1/N^2")
+    perm_t, perm_e = rng.permutation(T), rng.permutation(E)
+    close(oracle.aux_loss(a[perm_t][:, perm_e], cnt[perm_e], K, 0.3, 40, lib=lib), la,
+          what="relabel")
+    # brute force: the double sum over tokens and experts, term by term
+    want = sum(a[t, i] * cnt[i] for t in range(T) for i in range(E)) * 0.3 * E / (40 * 40 * K)
+    close(la, want, what="double sum")
+
+
+def pin_aux_loss_fd(lib):
+    """The gradient of the loss equals its central finite difference in
+    every score (the loss is linear, so the difference is exact up to
+    rounding), scaled by grad_loss."""
+    rng = np.random.default_rng(13)
+    T, E, K, coeff, N = 5, 6, 2, 0.05, 12
+    sc = rng.random((T, E))
+    cnt = rng.integers(0, 9, E)
+    d = oracle.aux_loss_bwd(-1.5, cnt, T, K, coeff, N, lib=lib)
+    h = 1e-3
+    fd = np.empty_like(sc)
+    for t in range(T):
+        for i in range(E):
+            up, dn = sc.copy(), sc.copy()
+            up[t, i] += h
+            dn[t, i] -= h
+            fd[t, i] = (oracle.aux_loss(up, cnt, K, coeff, N, lib=lib) -
+                        oracle.aux_loss(dn, cnt, K, coeff, N, lib=lib)) / (2 * h)
+    close(d, -1.5 * fd, rtol=1e-9, atol=1e-13, what="aux loss fd")
+
+
 PINS = [pin_golden, pin_score_library, pin_topk_bruteforce,
         pin_groups_bruteforce, pin_renorm_identities, pin_scale_linearity,
         pin_backward_fd, pin_aux_backward_fd, pin_backward_invariants,
-        pin_rows_independent, pin_margin]
+        pin_rows_independent, pin_margin, pin_tokens_per_expert,
+        pin_aux_loss_closed_forms, pin_aux_loss_fd]

@@ -66,6 +66,19 @@ MUTANTS = [
     ("aux_bwd_B_unweighted", "B += gr[i] * sr[i];", "B += sr[i];", 1),
     ("aux_bwd_raw_sigmoid", "dr[i] = gr[i] * sr[i] * (1.0 - sr[i]);",
      "dr[i] = gr[i] * sr[i];", 0),
+    ("tokens_row_offset", "counts[i] += map[t * E + i] ? 1 : 0;",
+     "counts[i] += map[i] ? 1 : 0;", 0),
+    ("tokens_not_reset", "counts[i] = 0;", "counts[i] = counts[i];", 0),
+    ("loss_no_E", "*loss = coeff * (double)E /", "*loss = coeff * 1.0 /", 0),
+    ("loss_N_not_squared", "/ ((double)N * (double)N * (double)K) * acc;",
+     "/ ((double)N * (double)K) * acc;", 0),
+    ("loss_no_K", "/ ((double)N * (double)N * (double)K) * acc;",
+     "/ ((double)N * (double)N) * acc;", 0),
+    ("loss_counts_ignored", "acc += (double)counts[i] * col;", "acc += col;", 0),
+    ("loss_col_row_offset", "col += scores[t * E + i];", "col += scores[i];", 0),
+    ("loss_bwd_counts_ignored", "(double)counts[i] /\n", "1.0 /\n", 0),
+    ("loss_bwd_grad_dropped", "grad_scores[t * E + i] = grad_loss * coeff",
+     "grad_scores[t * E + i] = coeff", 0),
     ("margin_sign", "gap = work[K - 1].key - work[K].key;",
      "gap = work[K].key - work[K - 1].key;", 0),
 ]

@@ -406,15 +406,20 @@ int oracle_aux_loss(const double *scores, const int64_t *counts, int64_t T,
     int64_t t;
     int i;
     double acc = 0.0;
+    double *col;
 
     if (T < 0 || E < 1 || N < 1 || K < 1)
         return -1;
-    for (i = 0; i < E; i++) {
-        double col = 0.0;
-        for (t = 0; t < T; t++)
-            col += scores[t * E + i];
-        acc += (double)counts[i] * col;
-    }
+    col = calloc((size_t)E, sizeof(double));
+    if (!col)
+        return -1;
+    /* column sums, each over the tokens in order (row-major walk) */
+    for (t = 0; t < T; t++)
+        for (i = 0; i < E; i++)
+            col[i] += scores[t * E + i];
+    for (i = 0; i < E; i++)
+        acc += (double)counts[i] * col[i];
+    free(col);
     *loss = coeff * (double)E / ((double)N * (double)N * (double)K) * acc;
     return 0;
 }

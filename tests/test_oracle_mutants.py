@@ -74,8 +74,8 @@ MUTANTS = [
      "/ ((double)N * (double)K) * acc;", 0),
     ("loss_no_K", "/ ((double)N * (double)N * (double)K) * acc;",
      "/ ((double)N * (double)N) * acc;", 0),
-    ("loss_counts_ignored", "acc += (double)counts[i] * col;", "acc += col;", 0),
-    ("loss_col_row_offset", "col += scores[t * E + i];", "col += scores[i];", 0),
+    ("loss_counts_ignored", "acc += (double)counts[i] * col[i];", "acc += col[i];", 0),
+    ("loss_col_row_offset", "col[i] += scores[t * E + i];", "col[i] += scores[i];", 0),
     ("loss_bwd_counts_ignored", "(double)counts[i] /\n", "1.0 /\n", 0),
     ("loss_bwd_grad_dropped", "grad_scores[t * E + i] = grad_loss * coeff",
      "grad_scores[t * E + i] = coeff", 0),

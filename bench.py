@@ -23,7 +23,6 @@ Prints one JSON line.  --gpus above 1 exits: this router is benchmarked on
 one GPU.
 """
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -37,19 +36,46 @@ METRIC = "effective HBM GB/s (and % of 8 TB/s) for router fwd/bwd at T=8192, E/K
 PEAK_GBPS = 8000.0          # MI355X HBM3E
 BYTES_PER_ELEM = {"topk_fwd": 13, "topk_bwd": 13, "aux_fwd": 13, "aux_bwd": 12}
 BF16_BYTES_PER_ELEM = {"topk_fwd": 9, "topk_bwd": 9, "aux_fwd": 9, "aux_bwd": 8}
+# Load-balancing loss passes (tokens per expert from the aux map, the loss over
+# the aux scores, its gradient): bytes per element of [T,E] plus per-expert
+# and scalar terms, fp32 scores.
+LOSS_KINDS = ["tokens_per_expert", "aux_loss_fwd", "aux_loss_bwd"]
+
+
+def loss_bytes(kind, T, E, esz):
+    if kind == "tokens_per_expert":
+        return T * E * 1 + E * 8           # map read, counts written
+    return T * E * esz + E * 8 + 4         # scores read (or grad written), counts, scalar
+
+
 # GPU kernel symbol of each pass: the top-k and aux passes share kernels, so
 # a profiler reports one average per symbol over both passes.
 KERNEL_SYMBOL = {"topk_fwd": "fwd_kernel", "topk_bwd": "bwd_kernel",
-                 "aux_fwd": "fwd_kernel", "aux_bwd": "bwd_kernel"}
+                 "aux_fwd": "fwd_kernel", "aux_bwd": "bwd_kernel",
+                 "tokens_per_expert": "count_kernel", "aux_loss_fwd": "loss_kernel",
+                 "aux_loss_bwd": "loss_bwd_kernel"}
 # B300 figures of the fused-router page for this exact shape (context only).
 PAGE_B300_GBPS = {"topk_fwd": 964, "topk_bwd": 2766, "aux_fwd": 891, "aux_bwd": 4201}
 
 
-def kernel_source_hash():
+# Sources each kernel symbol is built from (for the freshness check of the
+# committed counter summaries).
+_ROUTER_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_kernels.h",
+                   "router_launch.h", "router_params.h", "router_lpt16.hip", "router_lpt32.hip",
+                   "router_lpt64a.hip", "router_lpt64b.hip", "router_lpt64c.hip",
+                   "router_scalar.hip"]
+_LOSS_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",
+                 "router_loss.hip"]
+SYMBOL_SOURCES = {"fwd_kernel": _ROUTER_SOURCES, "bwd_kernel": _ROUTER_SOURCES,
+                  "loss_kernel": _LOSS_SOURCES, "count_kernel": _LOSS_SOURCES,
+                  "loss_bwd_kernel": _LOSS_SOURCES}
+
+
+def kernel_source_hash(symbol="fwd_kernel"):
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "score_function_top_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+    for name in sorted(SYMBOL_SOURCES[symbol]):
+        with open(os.path.join(ROOT, "score_function_top_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -65,7 +91,7 @@ def read_traffic(symbol):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    if vals.get("kernel_source_hash") != kernel_source_hash(symbol):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -177,6 +203,60 @@ def run_sweep(torch, router, synth, np, steps):
     return out
 
 
+def run_configs(torch, router, synth, np, steps):
+    """Per-pass microseconds and effective GB/s of the five router workloads
+    (bias, group-limited and bf16 variants included), cold caches, launches
+    replayed from a HIP graph."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, wl in synth.WORKLOADS.items():
+        T, E, K = wl.T, wl.E, wl.K
+        sname = "softmax" if wl.score_fn == synth.SOFTMAX else "sigmoid"
+        tdt = torch.float32 if wl.dtype == synth.F32 else torch.bfloat16
+        esz = 4 if wl.dtype == synth.F32 else 2
+
+        def host(arr):
+            a = np.ascontiguousarray(arr)
+            if wl.dtype == synth.F32:
+                return torch.from_numpy(a)
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+
+        x, g = host(wl.logits()[0]).to(dev), host(wl.grad()[0]).to(dev)
+        bias = wl.bias()
+        bd = None if bias is None else torch.from_numpy(bias).to(dev)
+        set_bytes = T * E * (4 * esz + 4 + 1)
+        n = max(4, -(-(2 << 30) // set_bytes))
+        sets = [{"x": x.clone(), "g": g.clone(), "p": torch.empty_like(x),
+                 "dx": torch.empty_like(x),
+                 "i": torch.empty(T, E, dtype=torch.float32, device=dev),
+                 "m": torch.empty(T, E, dtype=torch.bool, device=dev)} for _ in range(n)]
+        calls = {
+            "topk_fwd": lambda st: router.router_topk_fwd(
+                st["x"], K, sname, wl.renorm, wl.num_groups, wl.group_topk, wl.scaling_factor,
+                bd, out=(st["p"], st["m"], st["i"])),
+            "topk_bwd": lambda st: router.router_topk_bwd(
+                st["g"], st["i"], st["m"], K, sname, wl.renorm, wl.scaling_factor, out=st["dx"]),
+            "aux_fwd": lambda st: router.router_aux_scores(
+                st["x"], K, sname, wl.aux_renorm, out=(st["p"], st["m"], st["i"])),
+            "aux_bwd": lambda st: router.router_aux_scores_bwd(
+                st["g"], st["i"], sname, wl.aux_renorm, out=st["dx"]),
+        }
+        kinds = ["topk_fwd", "topk_bwd"] + (["aux_fwd", "aux_bwd"] if wl.aux else [])
+        bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
+        cell = {}
+        for kind in kinds:
+            if kind.endswith("bwd"):
+                for st in sets:
+                    calls[kind.replace("bwd", "fwd")](st)
+            f = calls[kind]
+            us = graph_us_per_launch(torch, [lambda st=sets[i % n]: f(st) for i in range(steps)])
+            nb = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None) else 0)
+            cell[kind] = {"us": round(us, 2), "GBps": round(nb / us / 1e3, 1)}
+        out[name] = cell
+        del sets, x, g
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,7 +268,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="oracle sample size in tokens (0: the whole batch)")
-    ap.add_argument("--only", choices=["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"],
+    ap.add_argument("--only", choices=["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"] + LOSS_KINDS,
                     help="time only this kernel kind (for profiler runs)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the T=8192 E/K sweep object")
@@ -241,6 +321,12 @@ def main():
         return s
 
     sets = [new_set() for _ in range(n_sets)]
+    ws_bytes = router.router_aux_loss_workspace_bytes(T, E)
+    for s in sets:
+        s["cnt"] = torch.zeros(E, dtype=torch.int64, device=dev)
+        s["loss"] = torch.empty((), dtype=torch.float32, device=dev)
+        s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
 
     def launch(kind, s):
         if kind == "topk_fwd":
@@ -253,18 +339,28 @@ def main():
         elif kind == "aux_fwd":
             router.router_aux_scores(s["x"], K, sname, wl.aux_renorm,
                                      out=(s["ascores"], s["amap"], s["ainter"]))
-        else:
+        elif kind == "aux_bwd":
             router.router_aux_scores_bwd(s["ag"], s["ainter"], sname, wl.aux_renorm,
                                          out=s["adx"])
+        elif kind == "tokens_per_expert":
+            router.router_tokens_per_expert(s["amap"], out=s["cnt"])
+        elif kind == "aux_loss_fwd":
+            router.router_aux_loss_fwd(s["ascores"], s["cnt"], T, K, synth.AUX_LOSS_COEFF,
+                                       out=s["loss"], workspace=s["ws"])
+        else:   # aux_loss_bwd: the gradient lands in the aux-backward output buffer
+            router.router_aux_loss_bwd(grad_loss, s["cnt"], T, T, K, synth.AUX_LOSS_COEFF,
+                                       dtype=tdt, out=s["adx"])
 
-    all_kinds = ["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"]
-    kinds = [args.only] if args.only else all_kinds
+    all_kinds = ["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"] + LOSS_KINDS
+    step_kinds = all_kinds[:4]
+    kinds = [args.only] if args.only else step_kinds
     # kernel k of step i works on set (i + k) % n: with n >= 4 every input was
     # last touched a full rotation of other buffers earlier (the backward
     # passes read the forward outputs of earlier steps)
     for s in sets:                       # produce every set's forward outputs
         launch("topk_fwd", s)
         launch("aux_fwd", s)
+        launch("tokens_per_expert", s)
     torch.cuda.synchronize()
 
     def step(i):
@@ -295,7 +391,8 @@ def main():
     # ---- per-kernel average launch duration: K back-to-back launches of one
     # kind (rotating sets, as in the step), one event pair around them
     per_kernel_us = {}
-    for kind in kinds:
+    timed_kinds = kinds if args.only else step_kinds + LOSS_KINDS
+    for kind in timed_kinds:
         k0 = all_kinds.index(kind)
         for i in range(3):
             launch(kind, sets[(i + k0) % n_sets])
@@ -311,12 +408,16 @@ def main():
     bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
     kern = {}
     for kind in kinds:
-        nbytes = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None) else 0)
+        if kind in LOSS_KINDS:
+            nbytes = loss_bytes(kind, T, E, esz)
+        else:
+            nbytes = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None)
+                                          else 0)
         avg = per_kernel_us[kind]
         kern[kind] = {"us_avg": round(avg, 2), "algo_bytes": nbytes,
                       "GBps": round(nbytes / avg / 1e3, 1),
                       "frac_of_peak": round(nbytes / avg / 1e3 / PEAK_GBPS, 4)}
-        if args.workload == "c4_softmax_2304x36":
+        if args.workload == "c4_softmax_2304x36" and kind in PAGE_B300_GBPS:
             kern[kind]["page_b300_GBps_context"] = PAGE_B300_GBPS[kind]
     step_bytes = sum(k["algo_bytes"] for k in kern.values())
     ms_per_step = total_ms / args.steps
@@ -375,13 +476,41 @@ def main():
         "kernels": kern,
         "wall_s_timed_region": round(t_wall, 4),
         "device": torch.cuda.get_device_name(0),
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": {"router": kernel_source_hash("fwd_kernel"),
+                               "loss": kernel_source_hash("loss_kernel")},
     }
+    if not args.only:
+        loss = {}
+        for kind in LOSS_KINDS:
+            nb = loss_bytes(kind, T, E, esz)
+            avg = per_kernel_us[kind]
+            k0 = all_kinds.index(kind)
+            g_us = graph_us_per_launch(
+                torch, [lambda i=i: launch(kind, sets[(i + k0) % n_sets])
+                        for i in range(args.steps)])
+            sym = KERNEL_SYMBOL[kind]
+            loss[kind] = {"kernels": (["zero_counts_kernel"] if sym == "count_kernel" else [])
+                          + [sym] + (["loss_final_kernel"] if sym == "loss_kernel" else []),
+                          "us_avg": round(avg, 2), "us_graph": round(g_us, 2),
+                          "algo_bytes": nb, "GBps": round(nb / avg / 1e3, 1),
+                          "GBps_graph": round(nb / g_us / 1e3, 1),
+                          "frac_of_peak": round(nb / avg / 1e3 / PEAK_GBPS, 4),
+                          "traffic": read_traffic(sym) if not args.warm else None}
+        out["aux_loss"] = loss
+        out["aux_loss_note"] = (
+            "load-balancing loss passes on the same workload (not part of the step): "
+            "tokens per expert from the aux map, loss over the fp32 aux scores, and its "
+            "gradient [T,E]; us_avg from back-to-back launches (HIP events on the launch "
+            "stream), us_graph from a replayed HIP graph; a pass's time covers all of its "
+            "kernels")
     if copy:
         out["copy_calibration"] = copy
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens or T)
     if not args.no_sweep and not args.only:
+        out["configs"] = run_configs(torch, router, synth, np, max(10, args.steps // 4))
+        out["configs_note"] = ("the five router workloads (c1..c5), cold, launches replayed "
+                               "from a HIP graph")
         t0 = time.perf_counter()
         out["sweep_GBps"] = run_sweep(torch, router, synth, np, max(10, args.steps // 4))
         out["sweep_note"] = (f"T=8192, per-pass effective GB/s, cold (rotating sets), launches "

@@ -5,7 +5,9 @@
  * Optimize fused router forward/backward kernels" (NVIDIA TransformerEngine
  * pull request 3012, "Summary"): fused_topk_with_score_function and
  * fused_score_for_moe_aux_loss, each with a forward and a backward, as
- * hand-written HIP kernels.
+ * hand-written HIP kernels; and the load-balancing loss that consumes the
+ * aux scores (the page's fused_moe_aux_loss, "Files changed"), with the
+ * tokens-per-expert counts it needs.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -19,6 +21,10 @@
  *           ROUTER_ERR_INVALID_ARG); when every array is 16-byte aligned
  *           and E is a multiple of 4 the kernels use vector loads and
  *           stores, otherwise element-wise ones (same results).
+ *           router_aux_loss_fwd takes a caller-owned device workspace of
+ *           router_aux_loss_workspace_bytes(T, E) bytes or more, with any
+ *           contents; it is scratch for the duration of the call's kernels
+ *           and must not be shared by calls that may run concurrently.
  * Dtypes.   `dtype` (router_dtype) is the storage type of logits, probs,
  *           scores and gradients.  intermediate is always fp32 and the
  *           routing map is one byte per element holding 0 or 1 (a torch
@@ -37,6 +43,7 @@
 #ifndef SCORE_FUNCTION_TOP_AMD_ROUTER_H
 #define SCORE_FUNCTION_TOP_AMD_ROUTER_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -152,6 +159,64 @@ router_status router_aux_scores_bwd(const void *grad_scores,
                                     int64_t T, int32_t E, int score_fn,
                                     int renorm, void *grad_logits,
                                     void *hip_stream);
+
+/*
+ * Load-balancing aux loss.  Passage: the fused-router page, "Files
+ * changed": fused_moe_aux_loss, the kernel that consumes the aux scores.
+ * The page does not state the loss; the one implemented is the
+ * Switch-Transformer balancing loss extended to top-K routing,
+ *   L = coeff * E / (N^2 K) * sum_i n_i * sum_t scores[t,i],
+ * where n_i = tokens_per_expert[i] is the number of tokens routed to expert
+ * i among N = total_tokens tokens (n and N may cover more tokens than the
+ * T local rows of `scores`, e.g. after summing the counts over ranks).
+ * Its gradient is dL/dscores[t,i] = coeff * E * n_i / (N^2 K).
+ *
+ * The loss is summed in fp64 in an order fixed by (T, E) alone, so it is
+ * reproducible bit for bit, and rounded to fp32 once.
+ */
+
+/* Bytes of workspace router_aux_loss_fwd needs for T rows of E experts (at
+ * least 256); 0 when T or E is out of range. */
+size_t router_aux_loss_workspace_bytes(int64_t T, int32_t E);
+
+/*
+ * router_tokens_per_expert -- tokens_per_expert[i] = number of rows t of
+ * routing_map [T,E] (uint8) with a nonzero byte at (t, i); int64 [E] out.
+ * Exact (integer atomics).  T == 0 writes zeros.  Errors: E < 1 or T < 0
+ * INVALID_ARG, E > ROUTER_MAX_EXPERTS or T > 2^32 - 1 UNSUPPORTED, T*E
+ * bytes overflowing OVERFLOW; null pointers or counts not 8-byte aligned
+ * INVALID_ARG.
+ */
+router_status router_tokens_per_expert(const uint8_t *routing_map,
+                                       int64_t T, int32_t E,
+                                       int64_t *tokens_per_expert,
+                                       void *hip_stream);
+
+/*
+ * router_aux_loss_fwd -- loss (one fp32 on the device) of scores [T,E]
+ * (`dtype`) with tokens_per_expert int64 [E] (device), total_tokens = N,
+ * K = topk and coeff.  T == 0 writes 0.  Errors (INVALID_ARG): N < 1,
+ * K < 1, coeff not finite, null pointers, misaligned arrays, a workspace
+ * smaller than router_aux_loss_workspace_bytes(T, E) or not 8-byte
+ * aligned; E > ROUTER_MAX_EXPERTS UNSUPPORTED.
+ */
+router_status router_aux_loss_fwd(const void *scores, int dtype, int64_t T,
+                                  int32_t E, const int64_t *tokens_per_expert,
+                                  int64_t total_tokens, int32_t K,
+                                  float coeff, float *loss, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
+/*
+ * router_aux_loss_bwd -- grad_scores [T,E] (`dtype`) =
+ * grad_loss[0] * coeff * E * n_i / (N^2 K), with grad_loss one fp32 on the
+ * device (the upstream gradient of the loss).  Arguments and errors as
+ * router_aux_loss_fwd; needs no workspace.  T == 0 is a no-op.
+ */
+router_status router_aux_loss_bwd(const float *grad_loss,
+                                  const int64_t *tokens_per_expert, int dtype,
+                                  int64_t T, int32_t E, int64_t total_tokens,
+                                  int32_t K, float coeff, void *grad_scores,
+                                  void *hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char *router_status_str(router_status s);

@@ -292,6 +292,34 @@ router_status bwd_common(const void *g, const float *s, const uint8_t *m, int dt
     return launch_bwd(c, dtype, score_fn, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
+// ------------------------------------------------------------ aux loss
+
+router_status check_loss_shape(int64_t T, int32_t E)
+{
+    if (T < 0 || E < 1)
+        return ROUTER_ERR_INVALID_ARG;
+    if (E > ROUTER_MAX_EXPERTS)
+        return ROUTER_ERR_UNSUPPORTED;
+    if (T > INT64_MAX / ((int64_t)E * 4))
+        return ROUTER_ERR_OVERFLOW;
+    return ROUTER_OK;
+}
+
+router_status check_loss_args(int dtype, int64_t N, int32_t K, float coeff)
+{
+    if (dtype != ROUTER_F32 && dtype != ROUTER_BF16)
+        return ROUTER_ERR_INVALID_ARG;
+    if (N < 1 || K < 1 || !std::isfinite(coeff))
+        return ROUTER_ERR_INVALID_ARG;
+    return ROUTER_OK;
+}
+
+// C = coeff * E / (N^2 K) in fp64.
+double loss_coeff(float coeff, int32_t E, int64_t N, int32_t K)
+{
+    return (double)coeff * (double)E / ((double)N * (double)N * (double)K);
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,6 +359,80 @@ router_status router_aux_scores_bwd(const void *grad_scores, const float *interm
 {
     return bwd_common(grad_scores, intermediate, nullptr, dtype, T, E, E > 0 ? E : 1, score_fn,
                       renorm, 1.0f, grad_logits, hip_stream);
+}
+
+size_t router_aux_loss_workspace_bytes(int64_t T, int32_t E)
+{
+    if (check_loss_shape(T, E) != ROUTER_OK)
+        return 0;
+    return aux_ws_bytes(T, E);
+}
+
+router_status router_tokens_per_expert(const uint8_t *routing_map, int64_t T, int32_t E,
+                                       int64_t *tokens_per_expert, void *hip_stream)
+{
+    router_status st = check_loss_shape(T, E);
+    if (st != ROUTER_OK)
+        return st;
+    if (T > (int64_t)UINT32_MAX)  // per-block counts are 32-bit
+        return ROUTER_ERR_UNSUPPORTED;
+    if (!tokens_per_expert || (T > 0 && !routing_map))
+        return ROUTER_ERR_INVALID_ARG;
+    if (!aligned(tokens_per_expert, 8))
+        return ROUTER_ERR_INVALID_ARG;
+    const int vec = E % 16 == 0 && aligned(routing_map, 16) ? 16
+                    : E % 4 == 0 && aligned(routing_map, 4)  ? 4
+                                                             : 1;
+    const hipError_t e = launch_count(routing_map, vec, count_geo(T, E), tokens_per_expert,
+                                      (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+router_status router_aux_loss_fwd(const void *scores, int dtype, int64_t T, int32_t E,
+                                  const int64_t *tokens_per_expert, int64_t total_tokens,
+                                  int32_t K, float coeff, float *loss, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream)
+{
+    router_status st = check_loss_shape(T, E);
+    if (st == ROUTER_OK)
+        st = check_loss_args(dtype, total_tokens, K, coeff);
+    if (st != ROUTER_OK)
+        return st;
+    if (!tokens_per_expert || !loss || !workspace || (T > 0 && !scores))
+        return ROUTER_ERR_INVALID_ARG;
+    const size_t ds = dsize(dtype);
+    if (!aligned(scores, ds) || !aligned(tokens_per_expert, 8) || !aligned(loss, 4) ||
+        !aligned(workspace, 8) || workspace_bytes < aux_ws_bytes(T, E))
+        return ROUTER_ERR_INVALID_ARG;
+    const bool vec = E % 4 == 0 && aligned(scores, 4 * ds);
+    const hipError_t e =
+        launch_loss(scores, dtype, vec, loss_geo(T, E), tokens_per_expert,
+                    loss_coeff(coeff, E, total_tokens, K), (double *)workspace, loss,
+                    (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+router_status router_aux_loss_bwd(const float *grad_loss, const int64_t *tokens_per_expert,
+                                  int dtype, int64_t T, int32_t E, int64_t total_tokens,
+                                  int32_t K, float coeff, void *grad_scores, void *hip_stream)
+{
+    router_status st = check_loss_shape(T, E);
+    if (st == ROUTER_OK)
+        st = check_loss_args(dtype, total_tokens, K, coeff);
+    if (st != ROUTER_OK)
+        return st;
+    if (T == 0)
+        return ROUTER_OK;
+    if (!grad_loss || !tokens_per_expert || !grad_scores)
+        return ROUTER_ERR_INVALID_ARG;
+    const size_t ds = dsize(dtype);
+    if (!aligned(grad_loss, 4) || !aligned(tokens_per_expert, 8) || !aligned(grad_scores, ds))
+        return ROUTER_ERR_INVALID_ARG;
+    const bool vec = E % 4 == 0 && aligned(grad_scores, 4 * ds);
+    const hipError_t e = launch_loss_bwd(grad_loss, tokens_per_expert, dtype, vec,
+                                         loss_geo(T, E), loss_coeff(coeff, E, total_tokens, K),
+                                         grad_scores, (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
 const char *router_status_str(router_status s)

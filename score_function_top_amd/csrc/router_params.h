@@ -61,6 +61,112 @@ struct Launch {
     hipStream_t stream;
 };
 
+// Column-stripe geometry of the aux-loss kernels (tokens per expert, the
+// loss and its gradient).  Lane l of a wave owns CPL = 1 << cpl_log2
+// consecutive columns, col0 = (stripe*LPR + l % LPR) * CPL, for every row it
+// visits, so per-column sums stay in registers; LPR (lanes per row) is the
+// smallest power of two with CPL*LPR >= E, at most 64, and a wave step
+// covers RPW = 64/LPR rows.  A block of `waves` waves covers one stripe of
+// CPL*LPR columns and a split of rows_per_split = waves*steps*RPW rows;
+// block b takes stripe b % nstripe and splits b / nstripe,
+// b / nstripe + gsplit, ...  gsplit is capped so the per-block partial
+// results stay small.  Everything depends on (T, E) only, so the order of
+// every sum is fixed.
+struct ColGeo {
+    int64_t T;
+    int E;
+    int waves;
+    int cpl_log2;
+    int lpr_log2;
+    int rpw_log2;
+    int steps;
+    int rows_per_split;
+    int nstripe;
+    int64_t nsplit;
+    int gsplit;
+};
+
+inline ColGeo col_geo(int64_t T, int E, int waves, int cpl_log2, int steps, int max_blocks)
+{
+    ColGeo g{};
+    g.T = T;
+    g.E = E;
+    g.waves = waves;
+    g.cpl_log2 = cpl_log2;
+    int lpr_log2 = 0;
+    while (lpr_log2 < 6 && (1 << (cpl_log2 + lpr_log2)) < E)
+        lpr_log2++;
+    g.lpr_log2 = lpr_log2;
+    g.rpw_log2 = 6 - lpr_log2;
+    g.steps = steps;
+    g.rows_per_split = waves * steps << g.rpw_log2;
+    const int width = 1 << (cpl_log2 + lpr_log2);
+    g.nstripe = (E + width - 1) / width;
+    g.nsplit = (T + g.rows_per_split - 1) / g.rows_per_split;
+    int64_t cap = max_blocks / g.nstripe;
+    if (cap < 1)
+        cap = 1;
+    g.gsplit = (int)(g.nsplit < cap ? g.nsplit : cap);
+    return g;
+}
+
+// Index maps of the geometry, shared by the kernels and the host-side
+// coverage check.  geo_width: columns per stripe; geo_col0: first of the
+// columns lane `lane` owns in `stripe`; geo_row_lane: the lane's row within
+// a wave step; geo_split_row: row (relative to its split) of step k of wave
+// w for that lane.
+constexpr int geo_width(const ColGeo &g) { return 1 << (g.cpl_log2 + g.lpr_log2); }
+constexpr int geo_col0(const ColGeo &g, int stripe, int lane)
+{
+    return ((stripe << g.lpr_log2) + (lane & ((1 << g.lpr_log2) - 1))) << g.cpl_log2;
+}
+constexpr int geo_row_lane(const ColGeo &g, int lane) { return lane >> g.lpr_log2; }
+constexpr int geo_split_row(const ColGeo &g, int w, int k, int row_lane)
+{
+    return ((w + g.waves * k) << g.rpw_log2) + row_lane;
+}
+
+// Count kernel: 8 waves, 16 map bytes per lane and row; loss kernels: 4
+// waves, 4 elements per lane and row.
+constexpr int kCountWaves = 8;
+constexpr int kCountCpl = 4;          // log2 of 16 columns per lane
+constexpr int kCountSteps = 16;       // row steps per wave and split (map)
+constexpr int kCountMaxBlocks = 1024;
+constexpr int kLossWaves = kWaves;
+constexpr int kLossCpl = 2;           // log2 of 4 columns per lane
+constexpr int kLossSteps = 16;        // row steps per wave and split (scores)
+constexpr int kLossMaxBlocks = 4096;
+
+inline ColGeo count_geo(int64_t T, int E)
+{
+    return col_geo(T, E, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks);
+}
+inline ColGeo loss_geo(int64_t T, int E)
+{
+    return col_geo(T, E, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks);
+}
+
+// Workspace of the loss kernel: one fp64 partial per block.
+inline size_t loss_ws_bytes(const ColGeo &g) { return (size_t)g.gsplit * g.nstripe * 8; }
+
+// Workspace of the loss for T rows of E experts (>= 256 bytes).
+inline size_t aux_ws_bytes(int64_t T, int E)
+{
+    size_t n = loss_ws_bytes(loss_geo(T, E));
+    n = (n + 255) / 256 * 256;
+    return n < 256 ? 256 : n;
+}
+
+// vec: 16 for 16-byte map loads (E % 16 == 0, 16-byte aligned map), 4 for
+// 4-byte loads (E % 4 == 0, 4-byte aligned), else 1 (byte loads).
+hipError_t launch_count(const uint8_t *map, int vec, const ColGeo &g, int64_t *counts,
+                        hipStream_t stream);
+hipError_t launch_loss(const void *scores, int dtype, bool vec, const ColGeo &g,
+                       const int64_t *counts, double C, double *ws, float *loss,
+                       hipStream_t stream);
+hipError_t launch_loss_bwd(const float *grad_loss, const int64_t *counts, int dtype, bool vec,
+                           const ColGeo &g, double C, void *grad_scores, hipStream_t stream);
+
 // Chunk counts built per lane-group width (see router_launch.h).
 constexpr int kNchLpt16[] = {1, 2, 4};
 constexpr int kNchLpt32[] = {1, 2, 4};

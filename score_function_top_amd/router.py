@@ -7,7 +7,8 @@ enqueued on the current stream of the input's device.  There is no CPU
 fallback: if librouter.so is not built, every call raises.
 
 Entry points carry the C names: router_topk_fwd, router_topk_bwd,
-router_aux_scores, router_aux_scores_bwd.
+router_aux_scores, router_aux_scores_bwd, router_tokens_per_expert,
+router_aux_loss_fwd, router_aux_loss_bwd, router_aux_loss_workspace_bytes.
 """
 import ctypes
 import os
@@ -53,8 +54,15 @@ def load():
     lib.router_topk_bwd.argtypes = [vp, vp, vp, ci, i64, i32, i32, ci, ci, f32, vp, vp]
     lib.router_aux_scores.argtypes = [vp, ci, i64, i32, i32, ci, ci, vp, vp, vp, vp]
     lib.router_aux_scores_bwd.argtypes = [vp, vp, ci, i64, i32, ci, ci, vp, vp]
+    lib.router_aux_loss_workspace_bytes.argtypes = [i64, i32]
+    lib.router_aux_loss_workspace_bytes.restype = ctypes.c_size_t
+    sz = ctypes.c_size_t
+    lib.router_tokens_per_expert.argtypes = [vp, i64, i32, vp, vp]
+    lib.router_aux_loss_fwd.argtypes = [vp, ci, i64, i32, vp, i64, i32, f32, vp, vp, sz, vp]
+    lib.router_aux_loss_bwd.argtypes = [vp, vp, ci, i64, i32, i64, i32, f32, vp, vp]
     for f in (lib.router_topk_fwd, lib.router_topk_bwd, lib.router_aux_scores,
-              lib.router_aux_scores_bwd, lib.router_set_topk_path_threshold):
+              lib.router_aux_scores_bwd, lib.router_set_topk_path_threshold,
+              lib.router_tokens_per_expert, lib.router_aux_loss_fwd, lib.router_aux_loss_bwd):
         f.restype = ci
     lib.router_set_topk_path_threshold.argtypes = [ci]
     lib.router_get_topk_path_threshold.argtypes = []
@@ -180,4 +188,78 @@ def router_aux_scores_bwd(grad_scores, intermediate, score_function="softmax",
     check(load().router_aux_scores_bwd(
         _ptr(grad_scores), _ptr(intermediate), _DTYPE[grad_scores.dtype], T, E,
         _SCORE[score_function], int(bool(renorm)), _ptr(dx), _stream(grad_scores)))
+    return dx
+
+
+def router_aux_loss_workspace_bytes(T, E):
+    """Workspace bytes of router_aux_loss_fwd for T rows of E experts (0 if
+    T, E are out of range)."""
+    return load().router_aux_loss_workspace_bytes(int(T), int(E))
+
+
+def _workspace(ws, T, E, device):
+    need = router_aux_loss_workspace_bytes(T, E)
+    if ws is None:
+        return torch.empty((max(need, 256),), dtype=torch.uint8, device=device)
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the input's device")
+    return ws
+
+
+def _counts(c, E, device):
+    if (not isinstance(c, torch.Tensor) or c.dtype != torch.int64 or c.shape != (E,)
+            or c.device != device or not c.is_contiguous()):
+        raise ValueError(f"tokens_per_expert must be a contiguous int64 [{E}] tensor on "
+                         f"{device}")
+    return c
+
+
+def router_tokens_per_expert(routing_map, out=None):
+    """Tokens routed to each expert: int64 [E] column counts of the bool (or
+    uint8) routing map [T,E]."""
+    if (not isinstance(routing_map, torch.Tensor) or routing_map.dim() != 2
+            or not routing_map.is_cuda or not routing_map.is_contiguous()
+            or routing_map.dtype not in (torch.bool, torch.uint8)):
+        raise ValueError("routing_map must be a contiguous bool/uint8 [T,E] GPU tensor")
+    T, E = routing_map.shape
+    dev = routing_map.device
+    counts = _out(out, (E,), torch.int64, dev, "tokens_per_expert")
+    check(load().router_tokens_per_expert(_ptr(routing_map), T, E, _ptr(counts),
+                                          _stream(routing_map)))
+    return counts
+
+
+def router_aux_loss_fwd(scores, tokens_per_expert, total_tokens, topk, coeff,
+                        out=None, workspace=None):
+    """Load-balancing loss coeff*E/(N^2 K) * sum_i n_i sum_t scores[t,i] as a
+    0-dim float32 tensor (N = total_tokens, n = tokens_per_expert)."""
+    T, E = _rows(scores, "scores")
+    dev = scores.device
+    counts = _counts(tokens_per_expert, E, dev)
+    loss = _out(out, (), torch.float32, dev, "loss")
+    ws = _workspace(workspace, T, E, dev)
+    check(load().router_aux_loss_fwd(
+        _ptr(scores), _DTYPE[scores.dtype], T, E, _ptr(counts), int(total_tokens),
+        int(topk), float(coeff), _ptr(loss), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(scores)))
+    return loss
+
+
+def router_aux_loss_bwd(grad_loss, tokens_per_expert, num_tokens, total_tokens, topk,
+                        coeff, dtype=torch.float32, out=None):
+    """Gradient of the loss with respect to the scores: [num_tokens, E] in
+    `dtype`, equal to grad_loss * coeff * E * n_i / (N^2 K) in column i."""
+    if (not isinstance(grad_loss, torch.Tensor) or grad_loss.dtype != torch.float32
+            or grad_loss.numel() != 1 or not grad_loss.is_cuda):
+        raise ValueError("grad_loss must be a one-element float32 GPU tensor")
+    dev = grad_loss.device
+    E = tokens_per_expert.shape[0] if isinstance(tokens_per_expert, torch.Tensor) else -1
+    counts = _counts(tokens_per_expert, E, dev)
+    if dtype not in _DTYPE:
+        raise ValueError("dtype must be float32 or bfloat16")
+    T = int(num_tokens)
+    dx = _out(out, (T, E), dtype, dev, "grad_scores")
+    check(load().router_aux_loss_bwd(
+        _ptr(grad_loss), _ptr(counts), _DTYPE[dtype], T, E, int(total_tokens), int(topk),
+        float(coeff), _ptr(dx), _stream(grad_loss)))
     return dx

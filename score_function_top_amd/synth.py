@@ -133,3 +133,29 @@ def sweep_workload(E, K, score_fn, T=8192):
                     T=T, E=E, K=K, score_fn=score_fn,
                     renorm=(score_fn == SIGMOID), aux=True, seed_logits=s,
                     seed_grad=s + 1, seed_bias=s + 2, seed_aux_grad=s + 3)
+
+
+# ------------------------------------------------------ aux-loss inputs
+#
+# The aux loss consumes aux scores [T,E] (probabilities, so non-negative and
+# of order 1/E) and per-expert token counts.  Isolated tests draw them
+# directly: scores U(0, 2/E) (mean 1/E, like a probability row) and routing
+# maps with exactly K ones per row at uniformly random columns.
+
+AUX_LOSS_COEFF = 1e-2    # a typical balancing-loss coefficient
+
+
+def prob_like(seed, T, E, dtype=F32):
+    """(storage, fp64) scores U(0, 2/E) rounded to the storage dtype."""
+    return storage(uniform(seed, (T, E), 0.0, 2.0 / E), dtype)
+
+
+def random_map(seed, T, E, K):
+    """uint8 [T,E], exactly K ones per row at columns drawn uniformly
+    without replacement (PCG64(seed))."""
+    rng = np.random.default_rng(seed)
+    m = np.zeros((T, E), np.uint8)
+    if T and K:
+        cols = np.argpartition(rng.random((T, E)), K - 1, axis=1)[:, :K]
+        np.put_along_axis(m, cols, 1, axis=1)
+    return m

@@ -148,3 +148,62 @@ def test_python_binding_rejects_host_tensors():
         router.router_aux_scores(x, 2)
     with pytest.raises(ValueError):
         router.router_topk_bwd(x, x, x.bool(), 2)
+
+
+def test_loss_geometry_covers_every_element(tmp_path):
+    """Host walk of every index the aux-loss kernels visit (same index maps
+    as the kernels): each element of [T,E] exactly once, all else masked."""
+    exe = tmp_path / "geo_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__",
+                    "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "score_function_top_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "native", "geo_check.cpp"), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+def test_aux_loss_workspace_query():
+    f = router.router_aux_loss_workspace_bytes
+    assert f(0, 1) == 256 and f(8192, 2304) >= 256
+    assert f(8192, 2304) % 256 == 0
+    assert f(-1, 8) == 0 and f(8, 0) == 0 and f(8, 4097) == 0 and f(1 << 62, 16) == 0
+
+
+def test_aux_loss_host_checks():
+    lib = router.load()
+    ws = router.router_aux_loss_workspace_bytes(8, 16)
+    tpe = lib.router_tokens_per_expert
+    assert tpe(P, 8, 0, P, None) == INV
+    assert tpe(P, -1, 16, P, None) == INV
+    assert tpe(P, 8, 4097, P, None) == UNS
+    assert tpe(P, 1 << 32, 16, P, None) == UNS
+    assert tpe(P, 1 << 62, 16, P, None) == OVF
+    assert tpe(None, 8, 16, P, None) == INV
+    assert tpe(P, 8, 16, None, None) == INV
+    assert tpe(P, 8, 16, P + 4, None) == INV              # counts not 8-byte aligned
+    fwd = lib.router_aux_loss_fwd
+    good = dict(s=P, dtype=0, T=8, E=16, n=P, N=8, K=2, c=0.01, loss=P, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return fwd(a["s"], a["dtype"], a["T"], a["E"], a["n"], a["N"], a["K"], a["c"],
+                   a["loss"], a["ws"], a["wsb"], None)
+    for kw, st in ((dict(dtype=2), INV), (dict(T=-1), INV), (dict(E=0), INV),
+                   (dict(E=5000), UNS), (dict(T=1 << 62), OVF), (dict(N=0), INV),
+                   (dict(K=0), INV), (dict(c=float("nan")), INV), (dict(c=float("inf")), INV),
+                   (dict(s=None), INV), (dict(n=None), INV), (dict(loss=None), INV),
+                   (dict(ws=None), INV), (dict(wsb=ws - 8), INV), (dict(s=P + 2), INV),
+                   (dict(dtype=1, s=P + 1), INV), (dict(loss=P + 2), INV)):
+        assert call(**kw) == st, kw
+    bwd = lib.router_aux_loss_bwd
+    assert bwd(P, P, 0, 8, 16, 0, 2, 0.01, P, None) == INV     # N = 0
+    assert bwd(P, P, 0, 8, 16, 8, 0, 0.01, P, None) == INV     # K = 0
+    assert bwd(P, P, 3, 8, 16, 8, 2, 0.01, P, None) == INV     # dtype
+    assert bwd(P, P, 0, 8, 5000, 8, 2, 0.01, P, None) == UNS
+    assert bwd(None, P, 0, 8, 16, 8, 2, 0.01, P, None) == INV
+    assert bwd(P, None, 0, 8, 16, 8, 2, 0.01, P, None) == INV
+    assert bwd(P, P, 0, 8, 16, 8, 2, 0.01, None, None) == INV
+    assert bwd(P, P, 1, 8, 16, 8, 2, 0.01, P + 1, None) == INV
+    assert bwd(P, P, 0, 8, 16, 8, 2, float("inf"), P, None) == INV
+    assert bwd(None, None, 0, 0, 16, 8, 2, 0.01, None, None) == OK   # T == 0: no-op

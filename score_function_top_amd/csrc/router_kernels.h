@@ -354,19 +354,25 @@ __device__ __forceinline__ void group_limit(float (&key)[NCH][4], const FwdParam
     float h = -INFINITY;
     if (lane < G && tok) {
         const float *gv = gscr + lane * (P + 1);
-        if (p.q == 1) {
-            float m1 = -INFINITY;
-            for (int i = 0; i < P; i++)
-                m1 = fmaxf(m1, gv[i]);
-            h = m1;
-        } else if (p.q == 2) {
-            float m1 = -INFINITY, m2 = -INFINITY;
+        if (p.q <= 4) {
+            // one pass keeping the 4 largest values, sorted (insertion by
+            // max/min from the bottom up); the sum takes the first q,
+            // largest first
+            float t0 = -INFINITY, t1 = -INFINITY, t2 = -INFINITY, t3 = -INFINITY;
             for (int i = 0; i < P; i++) {
                 const float v = gv[i];
-                m2 = fmaxf(m2, fminf(m1, v));
-                m1 = fmaxf(m1, v);
+                t3 = fmaxf(t3, fminf(t2, v));
+                t2 = fmaxf(t2, fminf(t1, v));
+                t1 = fmaxf(t1, fminf(t0, v));
+                t0 = fmaxf(t0, v);
             }
-            h = m1 + m2;
+            h = t0;
+            if (p.q > 1)
+                h = h + t1;
+            if (p.q > 2)
+                h = h + t2;
+            if (p.q > 3)
+                h = h + t3;
         } else {
             // q rounds, each taking the next largest (value, lower index)
             float acc = 0.0f, pv = INFINITY;
@@ -414,7 +420,7 @@ __device__ __forceinline__ void group_limit(float (&key)[NCH][4], const FwdParam
 // pruned sort, or the bit search when p.sel == SEL_BITS.  GROUPED kernels
 // add group-limited routing (p.G > 0).
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, bool GROUPED, bool VEC>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kBlock, GROUPED && VEC && NCH <= 4 ? 3 : 1)
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave

@@ -179,9 +179,16 @@ def test_edge_shapes(T, E, K, sf, renorm):
     (500, 256, 8, 8, 4, synth.BF16), (300, 256, 8, 8, 4, synth.F32), (200, 64, 6, 4, 2, synth.F32),
     (129, 512, 22, 16, 11, synth.F32), (64, 2304, 36, 36, 6, synth.F32),
     (90, 96, 12, 12, 4, synth.F32), (70, 160, 9, 10, 3, synth.F32), (50, 256, 8, 64, 8, synth.F32),
+    # q = 4 with groups of 64, 32 and 8 lanes; a group size that is no power-of-two
+    # number of lane quads (24 experts)
+    (100, 2048, 16, 8, 4, synth.F32), (100, 512, 16, 4, 4, synth.F32),
+    (257, 256, 16, 8, 4, synth.BF16), (60, 192, 8, 8, 4, synth.F32),
 ])
 @pytest.mark.parametrize("biased", [False, True])
 def test_groups(T, E, K, G, Kg, dtype, biased):
+    """Group-limited routing; shapes cover both group stages (registers:
+    group = 4 values of a power-of-two number of lanes and q <= 4; LDS:
+    otherwise)."""
     wl = edge_wl(T, E, K, synth.SIGMOID, True, bias=0.05 if biased else 0.0, G=G, Kg=Kg,
                  dtype=dtype, c=2.5, seed=11)
     run_fwd(wl)

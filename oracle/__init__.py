@@ -1,6 +1,6 @@
 """fp64 CPU oracle of the fused MoE router (score function + top-k, its
-backward, the aux-loss score variant, and the load-balancing loss over the
-aux scores).
+backward, the aux-loss score variant, the load-balancing loss over the aux
+scores, and decode-shape routing with (expert, token)-sorted expert maps).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code
@@ -56,9 +56,11 @@ def _load(path=None):
     lib.oracle_aux_loss.argtypes = [d, q, i64, i32, i64, i32, ctypes.c_double, d]
     lib.oracle_aux_loss_bwd.argtypes = [ctypes.c_double, q, i64, i32, i64, i32,
                                         ctypes.c_double, d]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_route_maps.argtypes = [d, i32, i32, i32, i32, i32, d, i32p, i32p, i32p, i32p, q]
     for f in (lib.oracle_topk_fwd, lib.oracle_topk_bwd, lib.oracle_aux_fwd,
               lib.oracle_aux_bwd, lib.oracle_tokens_per_expert, lib.oracle_aux_loss,
-              lib.oracle_aux_loss_bwd):
+              lib.oracle_aux_loss_bwd, lib.oracle_route_maps):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -235,4 +237,26 @@ def aux_loss_bwd(grad_loss, counts, T, K, coeff, total_tokens=None, lib=None):
     if lib.oracle_aux_loss_bwd(float(grad_loss), _p(c, ctypes.c_int64), T, E, N, K,
                                float(coeff), _p(out, ctypes.c_double)) != 0:
         raise OracleError("oracle_aux_loss_bwd rejected its arguments")
+    return out
+
+
+def route_maps(x, K, score_fn=SOFTMAX, renorm=False, lib=None):
+    """Decode routing with expert maps.  Returns a dict: weights [T,K] f64,
+    ids [T,K] int32, perm_to_unperm [T*K], unperm_to_perm [T*K],
+    perm_expert [T*K] (int32) and expert_offsets [E+1] int64."""
+    lib = lib or _load()
+    xx = _f64(x)
+    T, E = xx.shape
+    n = T * K
+    out = dict(weights=np.empty((T, K), np.float64), ids=np.empty((T, K), np.int32),
+               perm_to_unperm=np.empty((n,), np.int32), unperm_to_perm=np.empty((n,), np.int32),
+               perm_expert=np.empty((n,), np.int32), expert_offsets=np.empty((E + 1,), np.int64))
+    i32 = ctypes.c_int32
+    err = lib.oracle_route_maps(
+        _p(xx, ctypes.c_double), T, E, K, score_fn, int(bool(renorm)),
+        _p(out["weights"], ctypes.c_double), _p(out["ids"], i32),
+        _p(out["perm_to_unperm"], i32), _p(out["unperm_to_perm"], i32),
+        _p(out["perm_expert"], i32), _p(out["expert_offsets"], ctypes.c_int64))
+    if err:
+        raise OracleError("oracle_route_maps rejected its arguments")
     return out

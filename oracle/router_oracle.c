@@ -445,3 +445,95 @@ int oracle_aux_loss_bwd(double grad_loss, const int64_t *counts, int64_t T,
                                      ((double)N * (double)N * (double)K);
     return 0;
 }
+
+/* ------------------------------------------- decode routing + expert maps */
+
+typedef struct {
+    int expert;
+    int token;
+    int unpermuted; /* token + k * T */
+} pair_rec;
+
+static int pair_cmp(const void *pa, const void *pb)
+{
+    const pair_rec *a = (const pair_rec *)pa, *b = (const pair_rec *)pb;
+    if (a->expert != b->expert)
+        return a->expert < b->expert ? -1 : 1;
+    if (a->token != b->token)
+        return a->token < b->token ? -1 : 1;
+    return 0;
+}
+
+/*
+ * Decode-shape routing with expert maps (the onnxruntime page's fused
+ * softmax + top-k + expert-map kernel; the map layout of the TensorRT-LLM
+ * page's permutation maps).  Per token t: scores s = score_fn(x), the K
+ * experts with the largest logits in descending order (ties: lower index),
+ * ids[t*K + k] and weights[t*K + k] = s / (sum of the K selected scores)
+ * when renorm (skipped for sigmoid with K == 1), else s.  The T*K
+ * (token, slot) pairs, unpermuted index u = t + k*T, sorted by (expert,
+ * token) give the permuted order p: perm_to_unperm[p] = u,
+ * unperm_to_perm[u] = p, perm_expert[p] = expert, and expert_offsets[e] =
+ * number of pairs routed to experts below e (e = 0..E, last = T*K).
+ */
+int oracle_route_maps(const double *x, int T, int E, int K, int score_fn,
+                      int renorm, double *weights, int32_t *ids,
+                      int32_t *perm_to_unperm, int32_t *unperm_to_perm,
+                      int32_t *perm_expert, int64_t *expert_offsets)
+{
+    int t, k, j, p, n;
+    double *s;
+    keyed *work;
+    pair_rec *pairs;
+
+    if (T < 0 || E < 1 || K < 1 || K > E)
+        return -1;
+    n = T * K;
+    s = (double *)malloc(sizeof(double) * (size_t)E);
+    work = (keyed *)malloc(sizeof(keyed) * (size_t)E);
+    pairs = (pair_rec *)malloc(sizeof(pair_rec) * (size_t)(n > 0 ? n : 1));
+    if (!s || !work || !pairs) {
+        free(s);
+        free(work);
+        free(pairs);
+        return -1;
+    }
+    for (t = 0; t < T; t++) {
+        const double *xr = x + (int64_t)t * E;
+        double denom = 1.0;
+
+        score_row(xr, E, score_fn, s);
+        for (j = 0; j < E; j++) {
+            work[j].key = xr[j];
+            work[j].idx = j;
+        }
+        qsort(work, (size_t)E, sizeof(keyed), keyed_cmp);
+        if (renorm && (score_fn == ORACLE_SOFTMAX || K > 1)) {
+            denom = 0.0;
+            for (k = 0; k < K; k++)
+                denom += s[work[k].idx];
+        }
+        for (k = 0; k < K; k++) {
+            ids[t * K + k] = work[k].idx;
+            weights[t * K + k] = s[work[k].idx] / denom;
+            pairs[t + k * T].expert = work[k].idx;
+            pairs[t + k * T].token = t;
+            pairs[t + k * T].unpermuted = t + k * T;
+        }
+    }
+    qsort(pairs, (size_t)n, sizeof(pair_rec), pair_cmp);
+    for (p = 0; p < n; p++) {
+        perm_to_unperm[p] = pairs[p].unpermuted;
+        unperm_to_perm[pairs[p].unpermuted] = p;
+        perm_expert[p] = pairs[p].expert;
+    }
+    for (j = 0, p = 0; j <= E; j++) {
+        while (p < n && pairs[p].expert < j)
+            p++;
+        expert_offsets[j] = p;
+    }
+    free(s);
+    free(work);
+    free(pairs);
+    return 0;
+}

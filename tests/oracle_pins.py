@@ -116,7 +116,8 @@ def parse_golden(path):
                 vals = [float(Fraction(t)) for t in v.split()]
                 cur[k] = vals if len(vals) > 1 or k in (
                     "w", "s", "m", "g", "map", "probs", "inter", "scores",
-                    "dx", "bias", "counts", "dscore") else vals[0]
+                    "dx", "bias", "counts", "dscore", "ids", "weights", "perm_to_unperm",
+                    "unperm_to_perm", "perm_expert", "expert_offsets") else vals[0]
     return cases
 
 
@@ -132,6 +133,10 @@ def pin_golden(lib):
             what = f"{fn}:{c['case']}"
             if c["op"] == "aux_loss":
                 golden_aux_loss(lib, c, what)
+                n += 1
+                continue
+            if c["op"] == "route_maps":
+                golden_route_maps(lib, c, what)
                 n += 1
                 continue
             sf = SCORE[c["score"]]
@@ -166,7 +171,16 @@ def pin_golden(lib):
             else:
                 raise AssertionError(what)
             n += 1
-    assert n == 21, n
+    assert n == 24, n
+
+
+def golden_route_maps(lib, c, what):
+    T, E, K = int(c["T"]), int(c["E"]), int(c["K"])
+    x = np.log(np.array(c["w"])).reshape(T, E)
+    r = oracle.route_maps(x, K, SCORE[c["score"]], bool(c["renorm"]), lib=lib)
+    for f in ("ids", "perm_to_unperm", "unperm_to_perm", "perm_expert", "expert_offsets"):
+        assert (r[f].ravel() == np.array(c[f])).all(), (what, f, r[f])
+    close(r["weights"].ravel(), c["weights"], what=what + " weights")
 
 
 def golden_aux_loss(lib, c, what):
@@ -482,8 +496,66 @@ def pin_aux_loss_fd(lib):
     close(d, -1.5 * fd, rtol=1e-9, atol=1e-13, what="aux loss fd")
 
 
+def check_maps_structure(r, T, E, K, what=""):
+    """The maps are a permutation and its inverse, sorted by (expert,
+    token), with offsets equal to the cumulative expert histogram."""
+    n = T * K
+    p2u, u2p, pe, off = (r["perm_to_unperm"], r["unperm_to_perm"], r["perm_expert"],
+                         r["expert_offsets"])
+    assert sorted(p2u.tolist()) == list(range(n)), what
+    assert (u2p[p2u] == np.arange(n)).all(), what
+    tok = p2u % T if T else p2u
+    key = pe.astype(np.int64) * max(T, 1) + tok
+    assert (np.diff(key) > 0).all(), what
+    ids = r["ids"]
+    assert (pe == ids.T.ravel()[p2u]).all(), what
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    assert (off == np.concatenate([[0], np.cumsum(cnt)])).all(), what
+
+
+def pin_route_maps_bruteforce(lib):
+    """Selection against numpy's lexsort (logit descending, index
+    ascending), weights against scipy's softmax / logistic sigmoid, maps
+    against a lexsort of the pairs by (expert, token) and a bincount, on
+    random rows with heavy ties."""
+    rng = np.random.default_rng(21)
+    for T, E, K, sf, rn in ((1, 8, 3, oracle.SOFTMAX, False), (4, 512, 10, oracle.SOFTMAX, True),
+                            (3, 40, 6, oracle.SIGMOID, True), (4, 16, 16, oracle.SOFTMAX, True),
+                            (2, 7, 1, oracle.SIGMOID, True), (4, 64, 8, oracle.SIGMOID, False)):
+        x = rng.integers(-3, 4, (T, E)).astype(np.float64)   # many ties
+        r = oracle.route_maps(x, K, sf, rn, lib=lib)
+        s = scipy.special.softmax(x, axis=1) if sf == oracle.SOFTMAX else scipy.special.expit(x)
+        ids = np.stack([np.lexsort((np.arange(E), -x[t]))[:K] for t in range(T)])
+        assert (r["ids"] == ids).all(), (T, E, K)
+        w = np.take_along_axis(s, ids, 1)
+        if rn and (sf == oracle.SOFTMAX or K > 1):
+            w = w / w.sum(1, keepdims=True)
+        close(r["weights"], w, what="route weights")
+        exp = ids.T.ravel()                    # expert of unpermuted index u = t + k*T
+        tok = np.tile(np.arange(T), K)
+        order = np.lexsort((tok, exp))
+        assert (r["perm_to_unperm"] == order).all()
+        assert (r["perm_expert"] == exp[order]).all()
+        check_maps_structure(r, T, E, K)
+
+
+def pin_route_maps_vs_topk(lib):
+    """The selected set and weights equal the top-k forward's routing map
+    and probs (same scores, renorm rule, no scaling)."""
+    rng = np.random.default_rng(22)
+    for sf, rn in ((oracle.SOFTMAX, False), (oracle.SOFTMAX, True), (oracle.SIGMOID, True)):
+        x = rng.normal(0, 2, (4, 96))
+        r = oracle.route_maps(x, 9, sf, rn, lib=lib)
+        P, M, _, _ = oracle.topk_fwd(x, 9, sf, rn, lib=lib)
+        for t in range(4):
+            assert sorted(r["ids"][t].tolist()) == np.nonzero(M[t])[0].tolist()
+            close(r["weights"][t], P[t, r["ids"][t]], what="route vs topk")
+        assert (np.diff(np.take_along_axis(x, r["ids"].astype(np.int64), 1), axis=1) <= 0).all()
+
+
 PINS = [pin_golden, pin_score_library, pin_topk_bruteforce,
         pin_groups_bruteforce, pin_renorm_identities, pin_scale_linearity,
         pin_backward_fd, pin_aux_backward_fd, pin_backward_invariants,
         pin_rows_independent, pin_margin, pin_tokens_per_expert,
-        pin_aux_loss_closed_forms, pin_aux_loss_fd]
+        pin_aux_loss_closed_forms, pin_aux_loss_fd, pin_route_maps_bruteforce,
+        pin_route_maps_vs_topk]

@@ -79,6 +79,17 @@ MUTANTS = [
     ("loss_bwd_counts_ignored", "(double)counts[i] /\n", "1.0 /\n", 0),
     ("loss_bwd_grad_dropped", "grad_scores[t * E + i] = grad_loss * coeff",
      "grad_scores[t * E + i] = coeff", 0),
+    ("maps_sort_token_first", "if (a->expert != b->expert)\n        return a->expert < b->expert ? -1 : 1;\n    if (a->token != b->token)\n        return a->token < b->token ? -1 : 1;",
+     "if (a->token != b->token)\n        return a->token < b->token ? -1 : 1;\n    if (a->expert != b->expert)\n        return a->expert < b->expert ? -1 : 1;", 0),
+    ("maps_unpermuted_token_major", "pairs[t + k * T].unpermuted = t + k * T;",
+     "pairs[t + k * T].unpermuted = t * K + k;", 0),
+    ("maps_offsets_inclusive", "while (p < n && pairs[p].expert < j)",
+     "while (p < n && pairs[p].expert <= j)", 0),
+    ("maps_weights_first_only", "denom += s[work[k].idx];", "denom += s[work[0].idx];", 0),
+    ("maps_inverse_swapped", "unperm_to_perm[pairs[p].unpermuted] = p;",
+     "unperm_to_perm[p] = pairs[p].unpermuted;", 0),
+    ("maps_ids_unsorted_slot", "ids[t * K + k] = work[k].idx;",
+     "ids[t * K + k] = work[K - 1 - k].idx;", 0),
     ("margin_sign", "gap = work[K - 1].key - work[K].key;",
      "gap = work[K].key - work[K - 1].key;", 0),
 ]

@@ -257,6 +257,39 @@ def run_configs(torch, router, synth, np, steps):
     return out
 
 
+def run_decode_route(torch, router, synth, steps):
+    """Latency of decode-shape routing with expert maps (one workgroup per
+    call) at the onnxruntime page's shapes: T in 1..4 rows, E = 512 experts,
+    K in {1, 2, 4, 6, 8, 10}, softmax with renormalisation, fp32 logits.
+    us_graph: per call inside a replayed HIP graph of `steps` calls; us_eager:
+    `steps` back-to-back calls on the stream, one event pair (host launch
+    included when it is the bottleneck).  floor_us_graph: a one-element fill
+    kernel the same way, the cost of any dependent kernel on this device."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for T in (1, 2, 3, 4):
+        for K in (1, 2, 4, 6, 8, 10):
+            x = torch.from_numpy(synth.storage(synth.normal(9000 + 10 * T + K, (T, 512)),
+                                               synth.F32)[0]).to(dev)
+            res = router.router_route_maps(x, K, "softmax", True)
+            f = lambda: router.router_route_maps(x, K, "softmax", True, out=res)
+            g_us = graph_us_per_launch(torch, [f] * steps)
+            for _ in range(3):
+                f()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(steps):
+                f()
+            b.record()
+            torch.cuda.synchronize()
+            out[f"T{T}_K{K}"] = {"us_graph": round(g_us, 2),
+                                 "us_eager": round(a.elapsed_time(b) * 1e3 / steps, 2)}
+    one = torch.zeros(1, device=dev)
+    out["floor_us_graph"] = round(graph_us_per_launch(torch, [one.zero_] * steps), 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +303,8 @@ def main():
                     help="oracle sample size in tokens (0: the whole batch)")
     ap.add_argument("--only", choices=["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"] + LOSS_KINDS,
                     help="time only this kernel kind (for profiler runs)")
+    ap.add_argument("--only-decode-route", action="store_true",
+                    help="time only the decode routing (for profiler runs)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the T=8192 E/K sweep object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -284,6 +319,12 @@ def main():
     import numpy as np
     import torch
     from score_function_top_amd import router, synth
+
+    if args.only_decode_route:
+        torch.cuda.set_device(0)
+        print(json.dumps({"decode_route": run_decode_route(torch, router, synth, args.steps)}),
+              flush=True)
+        return
 
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -507,6 +548,11 @@ def main():
         out["copy_calibration"] = copy
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens or T)
+    if not args.only:
+        out["decode_route"] = run_decode_route(torch, router, synth, args.steps)
+        out["decode_route_note"] = (
+            "decode-shape routing with expert maps (one workgroup): microseconds per call, "
+            "T rows x E=512 experts x K, softmax renormalised, fp32")
     if not args.no_sweep and not args.only:
         out["configs"] = run_configs(torch, router, synth, np, max(10, args.steps // 4))
         out["configs_note"] = ("the five router workloads (c1..c5), cold, launches replayed "

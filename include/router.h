@@ -5,9 +5,12 @@
  * Optimize fused router forward/backward kernels" (NVIDIA TransformerEngine
  * pull request 3012, "Summary"): fused_topk_with_score_function and
  * fused_score_for_moe_aux_loss, each with a forward and a backward, as
- * hand-written HIP kernels; and the load-balancing loss that consumes the
- * aux scores (the page's fused_moe_aux_loss, "Files changed"), with the
- * tokens-per-expert counts it needs.
+ * hand-written HIP kernels; the load-balancing loss that consumes the aux
+ * scores (the page's fused_moe_aux_loss, "Files changed"), with the
+ * tokens-per-expert counts it needs; and decode-shape routing with the
+ * (expert, token)-sorted expert maps of "[CUDA] Add fused decode routing,
+ * single-pass finalize, and PDL overlap for NVFP4 QMoE" (onnxruntime pull
+ * request 33366).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -217,6 +220,43 @@ router_status router_aux_loss_bwd(const float *grad_loss,
                                   int64_t T, int32_t E, int64_t total_tokens,
                                   int32_t K, float coeff, void *grad_scores,
                                   void *hip_stream);
+
+/*
+ * router_route_maps -- decode-shape routing with expert maps.  Passage: the
+ * onnxruntime decode-routing page, Description item 1 (one launch does the
+ * softmax, the top-k and the (expert, token)-sorted expert maps for up to
+ * 4 rows, 512 experts, k in {1, 2, 4, 6, 8, 10}); the map layout follows
+ * the permutation maps of the TensorRT-LLM fused gather/finalize page
+ * (permuted row of unpermuted index token + k * num_rows, expert of each
+ * permuted row, first permuted row of each expert).
+ *
+ * Per token t (logits row [E] in `dtype`): s = softmax(x) or sigmoid(x);
+ * slots k = 0..K-1 hold the K largest logits in descending order (ties:
+ * lower expert index); topk_ids [T,K] int32 = their experts; topk_weights
+ * [T,K] fp32 = s, divided by the sum of the K selected s when renorm (not
+ * for sigmoid with K == 1).  The T*K pairs (t, k), unpermuted index
+ * u = t + k*T, sorted by (expert, token) give the permuted order p:
+ *   perm_to_unperm [T*K] int32:  u of permuted row p
+ *   unperm_to_perm [T*K] int32:  p of unpermuted index u
+ *   perm_expert    [T*K] int32:  expert of permuted row p
+ *   expert_offsets [E+1] int64:  first permuted row of each expert;
+ *                                expert_offsets[E] = T*K
+ * All integer outputs are exact.  One workgroup, one wave per row.
+ * Limits: 0 <= T <= ROUTER_ROUTE_MAX_ROWS, 1 <= K <= min(E,
+ * ROUTER_ROUTE_MAX_K), E <= ROUTER_ROUTE_MAX_EXPERTS (beyond:
+ * UNSUPPORTED).  T == 0 writes expert_offsets as zeros.  Errors
+ * (INVALID_ARG): dtype, score_fn, K outside [1, E], null or misaligned
+ * pointers (expert_offsets 8-byte aligned).
+ */
+#define ROUTER_ROUTE_MAX_ROWS 16
+#define ROUTER_ROUTE_MAX_EXPERTS 1024
+#define ROUTER_ROUTE_MAX_K 32
+router_status router_route_maps(const void *logits, int dtype, int32_t T,
+                                int32_t E, int32_t K, int score_fn, int renorm,
+                                float *topk_weights, int32_t *topk_ids,
+                                int32_t *perm_to_unperm,
+                                int32_t *unperm_to_perm, int32_t *perm_expert,
+                                int64_t *expert_offsets, void *hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char *router_status_str(router_status s);

@@ -435,6 +435,49 @@ router_status router_aux_loss_bwd(const float *grad_loss, const int64_t *tokens_
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
+router_status router_route_maps(const void *logits, int dtype, int32_t T, int32_t E, int32_t K,
+                                int score_fn, int renorm, float *topk_weights,
+                                int32_t *topk_ids, int32_t *perm_to_unperm,
+                                int32_t *unperm_to_perm, int32_t *perm_expert,
+                                int64_t *expert_offsets, void *hip_stream)
+{
+    if (dtype != ROUTER_F32 && dtype != ROUTER_BF16)
+        return ROUTER_ERR_INVALID_ARG;
+    if (score_fn != ROUTER_SOFTMAX && score_fn != ROUTER_SIGMOID)
+        return ROUTER_ERR_INVALID_ARG;
+    if (T < 0 || E < 1 || K < 1 || K > E)
+        return ROUTER_ERR_INVALID_ARG;
+    if (T > ROUTER_ROUTE_MAX_ROWS || E > ROUTER_ROUTE_MAX_EXPERTS || K > ROUTER_ROUTE_MAX_K)
+        return ROUTER_ERR_UNSUPPORTED;
+    if (!expert_offsets || !aligned(expert_offsets, 8))
+        return ROUTER_ERR_INVALID_ARG;
+    if (T > 0 && (!logits || !topk_weights || !topk_ids || !perm_to_unperm || !unperm_to_perm ||
+                  !perm_expert))
+        return ROUTER_ERR_INVALID_ARG;
+    const size_t ds = dsize(dtype);
+    if (T > 0 && (!aligned(logits, ds) || !aligned(topk_weights, 4) || !aligned(topk_ids, 4) ||
+                  !aligned(perm_to_unperm, 4) || !aligned(unperm_to_perm, 4) ||
+                  !aligned(perm_expert, 4)))
+        return ROUTER_ERR_INVALID_ARG;
+    RouteParams p{};
+    p.x = logits;
+    p.weights = topk_weights;
+    p.ids = topk_ids;
+    p.perm_to_unperm = perm_to_unperm;
+    p.unperm_to_perm = unperm_to_perm;
+    p.perm_expert = perm_expert;
+    p.offsets = expert_offsets;
+    p.T = T;
+    p.E = E;
+    p.K = K;
+    p.score = score_fn;
+    p.renorm = renorm ? 1 : 0;
+    const bool vec = E % 4 == 0 && aligned(logits, 4 * ds);
+    return launch_route_maps(p, dtype, vec, (hipStream_t)hip_stream) == hipSuccess
+               ? ROUTER_OK
+               : ROUTER_ERR_HIP;
+}
+
 const char *router_status_str(router_status s)
 {
     switch (s) {

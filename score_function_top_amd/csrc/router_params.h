@@ -167,6 +167,28 @@ hipError_t launch_loss(const void *scores, int dtype, bool vec, const ColGeo &g,
 hipError_t launch_loss_bwd(const float *grad_loss, const int64_t *counts, int dtype, bool vec,
                            const ColGeo &g, double C, void *grad_scores, hipStream_t stream);
 
+// Decode-shape routing with expert maps (one workgroup, one wave per row).
+constexpr int kRouteMaxRows = 16;
+constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteMaxK = 32;
+
+struct RouteParams {
+    const void *x;            // logits [T,E], TIn
+    float *weights;           // [T,K]
+    int32_t *ids;             // [T,K]
+    int32_t *perm_to_unperm;  // [T*K]
+    int32_t *unperm_to_perm;  // [T*K]
+    int32_t *perm_expert;     // [T*K]
+    int64_t *offsets;         // [E+1]
+    int T;
+    int E;
+    int K;
+    int score;                // SCORE_*
+    int renorm;
+};
+
+hipError_t launch_route_maps(const RouteParams &p, int dtype, bool vec, hipStream_t stream);
+
 // Chunk counts built per lane-group width (see router_launch.h).
 constexpr int kNchLpt16[] = {1, 2, 4};
 constexpr int kNchLpt32[] = {1, 2, 4};

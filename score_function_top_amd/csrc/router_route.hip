@@ -1,0 +1,239 @@
+// router_route.hip -- decode-shape routing with expert maps on gfx950: per
+// token the score function and the K largest logits in order, then the
+// (expert, token)-sorted expert maps of all T*K (token, slot) pairs, in one
+// workgroup.
+//
+// Operation: the fused softmax + top-k + expert-map kernel of "[CUDA] Add
+// fused decode routing, single-pass finalize, and PDL overlap for NVFP4
+// QMoE" (onnxruntime pull request 33366, Description item 1: up to 4 rows,
+// 512 experts, k in {1, 2, 4, 6, 8, 10}), with the map layout of the
+// permutation maps in the TensorRT-LLM fused gather/finalize page
+// (unpermuted index = token + k * num_rows; expert of each permuted row;
+// first permuted row of each expert).  The maths is stated in
+// include/router.h.
+//
+// One wave per token (T <= 16 waves in the block).  Lane l holds elements
+// j = c*256 + 4*l + u.  Slot k is the k-th round of a wave-wide maximum of
+// the packed key ord(x) << 32 | ~j (larger logit first, ties to the lower
+// index); lane k keeps slot k.  The maps need no sort: each expert's LDS
+// word collects a bit per token that chose it, so the expert offsets are an
+// exclusive scan of the words' popcounts and pair (t, k) -> expert e lands
+// at offset[e] + popcount(word[e] & ((1 << t) - 1)), which is the
+// (expert, token) order because a token picks an expert at most once.
+#include <hip/hip_runtime.h>
+
+#include "router_io.h"
+#include "router_params.h"
+
+namespace rker {
+
+namespace {
+
+constexpr int kRouteMaxPairs = kRouteMaxRows * kRouteMaxK;
+
+__device__ __forceinline__ uint64_t route_key(float x, uint32_t j)
+{
+    return ((uint64_t)ord_key(x + 0.0f) << 32) | (uint32_t)~j;
+}
+
+template <int NCH, typename TIn, bool VEC>
+__global__ __launch_bounds__(kRouteMaxRows * 64) void route_maps_kernel(RouteParams p)
+{
+    __shared__ uint32_t tokmask[kRouteMaxExperts];  // bit t: token t chose expert e
+    __shared__ uint32_t offs[kRouteMaxExperts + 1];
+    __shared__ int32_t pair_expert[kRouteMaxPairs];  // by unpermuted index t + k*T
+    __shared__ uint32_t wave_tot[kRouteMaxRows];
+
+    const int T = p.T, E = p.E, K = p.K, n = T * K;
+    const int nthreads = (int)blockDim.x;
+    const int tid = (int)threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = lane_id();
+    for (int e = tid; e < E; e += nthreads)
+        tokmask[e] = 0;
+    __syncthreads();
+
+    // ---- one wave per token: scores, ordered top-K, weights
+    if (w < T) {
+        constexpr uint32_t sz = io<TIn>::kSize;
+        const rsrc_t r = make_rsrc((const char *)p.x + (int64_t)w * E * sz, (uint32_t)E * sz);
+        float key[NCH][4];
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            const int j0 = c * 256 + 4 * lane;
+            if constexpr (VEC) {
+                io<TIn>::load4(r, j0 < E ? (uint32_t)j0 * sz : kOOB, 0, key[c]);
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    key[c][u] = j0 < E ? key[c][u] : -INFINITY;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const bool ok = j0 + u < E;
+                    const float v = io<TIn>::load1(r, ok ? (uint32_t)(j0 + u) * sz : kOOB);
+                    key[c][u] = ok ? v : -INFINITY;
+                }
+            }
+        }
+        float mx = 0.0f, rz = 0.0f;
+        if (p.score == SCORE_SOFTMAX) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    m = fmaxf(m, key[c][u]);
+            mx = group_max<64>(m);
+            float z = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    z += exp_split(key[c][u] - mx);  // padding: exactly 0
+            rz = 1.0f / group_sum<64>(z);
+        }
+        // the lane's packed keys, sorted descending once (bitonic network);
+        // padding packs to 0, below every real key
+        constexpr int V = NCH * 4;
+        uint64_t lst[V];
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                lst[c * 4 + u] = key[c][u] == -INFINITY
+                                     ? 0ull
+                                     : route_key(key[c][u], (uint32_t)(c * 256 + 4 * lane + u));
+#pragma unroll
+        for (int k2 = 2; k2 <= V; k2 <<= 1)
+#pragma unroll
+            for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1)
+#pragma unroll
+                for (int i = 0; i < V; i++) {
+                    const int l2 = i ^ j2;
+                    if (l2 > i) {
+                        // descending where bit k2 of i is clear, ascending where set
+                        const bool desc = (i & k2) == 0;
+                        const uint64_t a = lst[i], b = lst[l2];
+                        const bool swap = desc ? (b > a) : (a > b);
+                        lst[i] = swap ? b : a;
+                        lst[l2] = swap ? a : b;
+                    }
+                }
+        // K ordered rounds: the wave maximum of the lanes' heads; the
+        // winning lane pops its head; lane k keeps slot k
+        int my_id = 0;
+        float my_s = 0.0f;
+        for (int k = 0; k < K; k++) {
+            const uint64_t best = group_max_u64<64>(lst[0]);
+            const bool win = lst[0] == best;
+#pragma unroll
+            for (int i = 0; i + 1 < V; i++)
+                lst[i] = win ? lst[i + 1] : lst[i];
+            lst[V - 1] = win ? 0ull : lst[V - 1];
+            const uint32_t jw = ~(uint32_t)best;
+            const float xw = ord_key_inv((uint32_t)(best >> 32));
+            const float sw = p.score == SCORE_SOFTMAX ? exp_split(xw - mx) * rz : sigmoid_fast(xw);
+            my_id = lane == k ? (int)jw : my_id;
+            my_s = lane == k ? sw : my_s;
+        }
+        float wgt = my_s;
+        if (p.renorm && (p.score == SCORE_SOFTMAX || K > 1)) {
+            // the selected scores in slot order, summed sequentially
+            float den = 0.0f;
+            for (int k = 0; k < K; k++)
+                den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+            wgt = my_s / den;
+        }
+        if (lane < K) {
+            const rsrc_t rw = make_rsrc(p.weights, (uint32_t)n * 4u);
+            const rsrc_t ri = make_rsrc(p.ids, (uint32_t)n * 4u);
+            const uint32_t o = (uint32_t)(w * K + lane) * 4u;
+            __builtin_amdgcn_raw_buffer_store_b32(as_u(wgt), rw, (int)o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)my_id, ri, (int)o, 0, 0);
+            pair_expert[w + lane * T] = my_id;
+            atomicOr(&tokmask[my_id], 1u << w);
+        }
+    }
+    __syncthreads();
+
+    // ---- offsets: exclusive scan of popcount(tokmask[e]) over e < E; thread
+    // t owns the contiguous run [t*m, t*m + m) of experts
+    const int nwaves = nthreads >> 6;
+    const int m = (E + nthreads - 1) / nthreads;  // <= kRouteMaxExperts / 64
+    const int e0 = tid * m;
+    uint32_t loc = 0;
+    for (int i = 0; i < m; i++)
+        loc += e0 + i < E ? (uint32_t)__builtin_popcount(tokmask[e0 + i]) : 0u;
+    const uint32_t incl = group_incl_scan<64>(loc);
+    if (lane == 63)
+        wave_tot[w] = incl;
+    __syncthreads();
+    uint32_t run = incl - loc;
+    for (int w2 = 0; w2 < w; w2++)
+        run += wave_tot[w2];
+    for (int i = 0; i < m; i++) {
+        if (e0 + i < E) {
+            offs[e0 + i] = run;
+            run += (uint32_t)__builtin_popcount(tokmask[e0 + i]);
+        }
+    }
+    if (tid == 0) {
+        uint32_t tot = 0;
+        for (int w2 = 0; w2 < nwaves; w2++)
+            tot += wave_tot[w2];
+        offs[E] = tot;  // = T*K
+    }
+    __syncthreads();
+
+    const rsrc_t ro = make_rsrc(p.offsets, (uint32_t)(E + 1) * 8u);
+    for (int e = tid; e <= E; e += nthreads) {
+        __attribute__((ext_vector_type(2))) uint32_t v2;
+        v2[0] = offs[e];
+        v2[1] = 0u;
+        __builtin_amdgcn_raw_buffer_store_b64(v2, ro, e * 8, 0, 0);
+    }
+    const rsrc_t rp2u = make_rsrc(p.perm_to_unperm, (uint32_t)n * 4u);
+    const rsrc_t ru2p = make_rsrc(p.unperm_to_perm, (uint32_t)n * 4u);
+    const rsrc_t rpe = make_rsrc(p.perm_expert, (uint32_t)n * 4u);
+    for (int u = tid; u < n; u += nthreads) {
+        const int e = pair_expert[u];
+        const int t = u % T;
+        const uint32_t pos = offs[e] + (uint32_t)__builtin_popcount(tokmask[e] & ((1u << t) - 1u));
+        __builtin_amdgcn_raw_buffer_store_b32(pos, ru2p, u * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)u, rp2u, (int)pos * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)e, rpe, (int)pos * 4, 0, 0);
+    }
+}
+
+template <int NCH>
+hipError_t route_nch(const RouteParams &p, int dtype, bool vec, hipStream_t stream)
+{
+    const dim3 grid(1), block(64 * (p.T > 0 ? p.T : 1));
+    if (dtype == 0) {
+        if (vec)
+            hipLaunchKernelGGL((route_maps_kernel<NCH, float, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((route_maps_kernel<NCH, float, false>), grid, block, 0, stream, p);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((route_maps_kernel<NCH, uint16_t, true>), grid, block, 0, stream,
+                               p);
+        else
+            hipLaunchKernelGGL((route_maps_kernel<NCH, uint16_t, false>), grid, block, 0, stream,
+                               p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_maps(const RouteParams &p, int dtype, bool vec, hipStream_t stream)
+{
+    if (p.E <= 256)
+        return route_nch<1>(p, dtype, vec, stream);
+    if (p.E <= 512)
+        return route_nch<2>(p, dtype, vec, stream);
+    return route_nch<4>(p, dtype, vec, stream);
+}
+
+}  // namespace rker

@@ -8,7 +8,8 @@ fallback: if librouter.so is not built, every call raises.
 
 Entry points carry the C names: router_topk_fwd, router_topk_bwd,
 router_aux_scores, router_aux_scores_bwd, router_tokens_per_expert,
-router_aux_loss_fwd, router_aux_loss_bwd, router_aux_loss_workspace_bytes.
+router_aux_loss_fwd, router_aux_loss_bwd, router_aux_loss_workspace_bytes,
+router_route_maps.
 """
 import ctypes
 import os
@@ -22,6 +23,7 @@ OK, ERR_INVALID_ARG, ERR_OVERFLOW, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 SOFTMAX, SIGMOID = 0, 1
 MAX_EXPERTS = 4096
+ROUTE_MAX_ROWS, ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 16, 1024, 32
 
 _SCORE = {"softmax": SOFTMAX, "sigmoid": SIGMOID, SOFTMAX: SOFTMAX,
           SIGMOID: SIGMOID}
@@ -60,6 +62,8 @@ def load():
     lib.router_tokens_per_expert.argtypes = [vp, i64, i32, vp, vp]
     lib.router_aux_loss_fwd.argtypes = [vp, ci, i64, i32, vp, i64, i32, f32, vp, vp, sz, vp]
     lib.router_aux_loss_bwd.argtypes = [vp, vp, ci, i64, i32, i64, i32, f32, vp, vp]
+    lib.router_route_maps.argtypes = [vp, ci, i32, i32, i32, ci, ci, vp, vp, vp, vp, vp, vp, vp]
+    lib.router_route_maps.restype = ci
     for f in (lib.router_topk_fwd, lib.router_topk_bwd, lib.router_aux_scores,
               lib.router_aux_scores_bwd, lib.router_set_topk_path_threshold,
               lib.router_tokens_per_expert, lib.router_aux_loss_fwd, lib.router_aux_loss_bwd):
@@ -263,3 +267,26 @@ def router_aux_loss_bwd(grad_loss, tokens_per_expert, num_tokens, total_tokens, 
         _ptr(grad_loss), _ptr(counts), _DTYPE[dtype], T, E, int(total_tokens), int(topk),
         float(coeff), _ptr(dx), _stream(grad_loss)))
     return dx
+
+
+def router_route_maps(logits, topk, score_function="softmax", renorm=False, out=None):
+    """Decode-shape routing with expert maps (T <= 16 rows, E <= 1024,
+    K <= 32).  Returns a dict of device tensors: topk_weights [T,K] float32,
+    topk_ids [T,K] int32, perm_to_unperm / unperm_to_perm / perm_expert
+    [T*K] int32 and expert_offsets [E+1] int64; `out` may pass the same
+    dict preallocated."""
+    T, E = _rows(logits, "logits")
+    K = int(topk)
+    dev = logits.device
+    n = T * K
+    shapes = {"topk_weights": ((T, K), torch.float32), "topk_ids": ((T, K), torch.int32),
+              "perm_to_unperm": ((n,), torch.int32), "unperm_to_perm": ((n,), torch.int32),
+              "perm_expert": ((n,), torch.int32), "expert_offsets": ((E + 1,), torch.int64)}
+    res = {k: _out(None if out is None else out.get(k), shp, dt, dev, k)
+           for k, (shp, dt) in shapes.items()}
+    check(load().router_route_maps(
+        _ptr(logits), _DTYPE[logits.dtype], T, E, K, _SCORE[score_function],
+        int(bool(renorm)), _ptr(res["topk_weights"]), _ptr(res["topk_ids"]),
+        _ptr(res["perm_to_unperm"]), _ptr(res["unperm_to_perm"]), _ptr(res["perm_expert"]),
+        _ptr(res["expert_offsets"]), _stream(logits)))
+    return res

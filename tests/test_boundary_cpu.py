@@ -207,3 +207,22 @@ def test_aux_loss_host_checks():
     assert bwd(P, P, 1, 8, 16, 8, 2, 0.01, P + 1, None) == INV
     assert bwd(P, P, 0, 8, 16, 8, 2, float("inf"), P, None) == INV
     assert bwd(None, None, 0, 0, 16, 8, 2, 0.01, None, None) == OK   # T == 0: no-op
+
+
+def test_route_maps_host_checks():
+    f = router.load().router_route_maps
+
+    def call(**kw):
+        a = dict(x=P, dtype=0, T=4, E=512, K=8, score=0, renorm=1, w=P, ids=P, p2u=P, u2p=P,
+                 pe=P, off=P)
+        a.update(kw)
+        return f(a["x"], a["dtype"], a["T"], a["E"], a["K"], a["score"], a["renorm"], a["w"],
+                 a["ids"], a["p2u"], a["u2p"], a["pe"], a["off"], None)
+    for kw, st in ((dict(dtype=2), INV), (dict(score=3), INV), (dict(T=-1), INV),
+                   (dict(E=0), INV), (dict(K=0), INV), (dict(K=513), INV),
+                   (dict(T=17), UNS), (dict(E=1025, K=4), UNS), (dict(K=33), UNS),
+                   (dict(x=None), INV), (dict(w=None), INV), (dict(ids=None), INV),
+                   (dict(p2u=None), INV), (dict(u2p=None), INV), (dict(pe=None), INV),
+                   (dict(off=None), INV), (dict(off=P + 4), INV), (dict(x=P + 2), INV),
+                   (dict(dtype=1, x=P + 1), INV), (dict(ids=P + 2), INV)):
+        assert call(**kw) == st, kw

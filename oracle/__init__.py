@@ -1,6 +1,7 @@
 """fp64 CPU oracle of the fused MoE router (score function + top-k, its
 backward, the aux-loss score variant, the load-balancing loss over the aux
-scores, and decode-shape routing with (expert, token)-sorted expert maps).
+scores, decode-shape routing with (expert, token)-sorted expert maps, and
+the routed top-k with the shared-expert sigmoid gate folded in).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code
@@ -58,9 +59,11 @@ def _load(path=None):
                                         ctypes.c_double, d]
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.oracle_route_maps.argtypes = [d, i32, i32, i32, i32, i32, d, i32p, i32p, i32p, i32p, q]
+    lib.oracle_topk_shared_gate.argtypes = [d, d, d, i64, i32, i32, i32, i32, i32,
+                                            ctypes.c_double, i32, i64, d, i32p]
     for f in (lib.oracle_topk_fwd, lib.oracle_topk_bwd, lib.oracle_aux_fwd,
               lib.oracle_aux_bwd, lib.oracle_tokens_per_expert, lib.oracle_aux_loss,
-              lib.oracle_aux_loss_bwd, lib.oracle_route_maps):
+              lib.oracle_aux_loss_bwd, lib.oracle_route_maps, lib.oracle_topk_shared_gate):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -260,3 +263,37 @@ def route_maps(x, K, score_fn=SOFTMAX, renorm=False, lib=None):
     if err:
         raise OracleError("oracle_route_maps rejected its arguments")
     return out
+
+
+def topk_shared_gate(x, hs, gw, K, renorm=True, scale=1.0, shared_base=None, ld=None,
+                     lib=None, threads=1):
+    """Routed softmax top-k plus shared-expert gates.  Returns (weights
+    [M, ld] f64, ids [M, ld] int32); columns >= K + S are left untouched
+    (NaN / -1 here)."""
+    lib = lib or _load()
+    xx, hh, ww = _f64(x), _f64(hs), _f64(gw)
+    M, E = xx.shape
+    H = hh.shape[1]
+    S = ww.shape[0]
+    assert hh.shape[0] == M and ww.shape[1] == H
+    base = E if shared_base is None else int(shared_base)
+    ld = K + S if ld is None else int(ld)
+    w = np.full((M, ld), np.nan)
+    ids = np.full((M, ld), -1, np.int32)
+
+    def run(a, b):
+        if b <= a:
+            return 0
+        return lib.oracle_topk_shared_gate(
+            _p(xx[a:b], ctypes.c_double), _p(hh[a:b], ctypes.c_double),
+            _p(ww, ctypes.c_double), b - a, E, H, K, S, int(bool(renorm)), float(scale),
+            base, ld, _p(w[a:b], ctypes.c_double), _p(ids[a:b], ctypes.c_int32))
+    if threads > 1 and M > threads:
+        step = -(-M // threads)
+        with ThreadPoolExecutor(threads) as ex:
+            errs = list(ex.map(lambda a: run(a, min(M, a + step)), range(0, M, step)))
+    else:
+        errs = [run(0, M)]
+    if any(errs):
+        raise OracleError("oracle_topk_shared_gate rejected its arguments")
+    return w, ids

@@ -537,3 +537,69 @@ int oracle_route_maps(const double *x, int T, int E, int K, int score_fn,
     free(pairs);
     return 0;
 }
+
+/* --------------------------------------- routed top-k + shared-expert gate */
+
+/*
+ * Routed softmax top-k with the shared-expert sigmoid gate folded in (the
+ * aiter page "[HIP] [Perf] Fold shared-expert gate GEMV into topk_softmax
+ * kernel": routed top-k weights and ids, then for each shared expert s the
+ * gate scale * sigmoid(hidden_states[m,:] . gate_weight[s,:]) with id
+ * shared_base + s, in the columns after the K routed ones).  Per token m:
+ *   slots k < K: the K largest gating logits in descending order (ties:
+ *   lower expert), weight = softmax score, divided by the sum of the K
+ *   selected scores when renorm;
+ *   slots K + s: weight = scale / (1 + exp(-sum_h hs[m,h] * gw[s,h])),
+ *   id = shared_base + s.
+ * weights/ids rows have stride ld >= K + S.
+ */
+int oracle_topk_shared_gate(const double *x, const double *hs, const double *gw,
+                            int64_t M, int E, int H, int K, int S, int renorm,
+                            double scale, int shared_base, int64_t ld,
+                            double *weights, int32_t *ids)
+{
+    int64_t m;
+    int j, k, s, h;
+    double *sc;
+    keyed *work;
+
+    if (M < 0 || E < 1 || H < 1 || K < 1 || K > E || S < 1 || ld < K + S)
+        return -1;
+    sc = (double *)malloc(sizeof(double) * (size_t)E);
+    work = (keyed *)malloc(sizeof(keyed) * (size_t)E);
+    if (!sc || !work) {
+        free(sc);
+        free(work);
+        return -1;
+    }
+    for (m = 0; m < M; m++) {
+        const double *xr = x + m * E;
+        double denom = 1.0;
+
+        score_row(xr, E, ORACLE_SOFTMAX, sc);
+        for (j = 0; j < E; j++) {
+            work[j].key = xr[j];
+            work[j].idx = j;
+        }
+        qsort(work, (size_t)E, sizeof(keyed), keyed_cmp);
+        if (renorm) {
+            denom = 0.0;
+            for (k = 0; k < K; k++)
+                denom += sc[work[k].idx];
+        }
+        for (k = 0; k < K; k++) {
+            weights[m * ld + k] = sc[work[k].idx] / denom;
+            ids[m * ld + k] = work[k].idx;
+        }
+        for (s = 0; s < S; s++) {
+            double dot = 0.0;
+            for (h = 0; h < H; h++)
+                dot += hs[m * H + h] * gw[(int64_t)s * H + h];
+            weights[m * ld + K + s] = scale / (1.0 + exp(-dot));
+            ids[m * ld + K + s] = shared_base + s;
+        }
+    }
+    free(sc);
+    free(work);
+    return 0;
+}

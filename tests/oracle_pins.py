@@ -117,7 +117,8 @@ def parse_golden(path):
                 cur[k] = vals if len(vals) > 1 or k in (
                     "w", "s", "m", "g", "map", "probs", "inter", "scores",
                     "dx", "bias", "counts", "dscore", "ids", "weights", "perm_to_unperm",
-                    "unperm_to_perm", "perm_expert", "expert_offsets") else vals[0]
+                    "unperm_to_perm", "perm_expert", "expert_offsets", "hs_ln",
+                    "gw") else vals[0]
     return cases
 
 
@@ -137,6 +138,10 @@ def pin_golden(lib):
                 continue
             if c["op"] == "route_maps":
                 golden_route_maps(lib, c, what)
+                n += 1
+                continue
+            if c["op"] == "topk_shared_gate":
+                golden_shared_gate(lib, c, what)
                 n += 1
                 continue
             sf = SCORE[c["score"]]
@@ -171,7 +176,18 @@ def pin_golden(lib):
             else:
                 raise AssertionError(what)
             n += 1
-    assert n == 24, n
+    assert n == 26, n
+
+
+def golden_shared_gate(lib, c, what):
+    E, H, K, S = int(c["E"]), int(c["H"]), int(c["K"]), int(c["S"])
+    x = np.log(np.array(c["w"])).reshape(-1, E)
+    hs = np.log(np.array(c["hs_ln"], dtype=np.float64).reshape(-1, H))
+    gw = np.array(c["gw"], dtype=np.float64).reshape(S, H)
+    w, ids = oracle.topk_shared_gate(x, hs, gw, K, bool(c["renorm"]), c["scale"],
+                                     int(c["base"]), lib=lib)
+    assert (ids.ravel() == np.array(c["ids"])).all(), (what, ids)
+    close(w.ravel(), c["weights"], what=what + " weights")
 
 
 def golden_route_maps(lib, c, what):
@@ -553,9 +569,53 @@ def pin_route_maps_vs_topk(lib):
         assert (np.diff(np.take_along_axis(x, r["ids"].astype(np.int64), 1), axis=1) <= 0).all()
 
 
+def pin_shared_gate_library(lib):
+    """Routed part against numpy lexsort and scipy softmax, gates against
+    scipy's expit of numpy's dot, on the page's test axes (S in {1, 2, 8},
+    renorm on/off, scale 0.5, M = 1 and 65), with a wider output row whose
+    extra columns stay untouched."""
+    rng = np.random.default_rng(31)
+    for M, E, H, K, S, rn, sc in ((1, 512, 64, 10, 1, True, 1.0), (65, 256, 48, 8, 2, False, 0.5),
+                                  (9, 64, 40, 6, 8, True, 0.5), (4, 20, 7, 20, 3, True, 2.0)):
+        x = rng.integers(-3, 4, (M, E)).astype(np.float64)      # ties
+        hs = rng.normal(0, 1, (M, H))
+        gw = rng.normal(0, 0.2, (S, H))
+        ld = K + S + 3
+        w, ids = oracle.topk_shared_gate(x, hs, gw, K, rn, sc, 1000, ld, lib=lib)
+        sm = scipy.special.softmax(x, axis=1)
+        top = np.stack([np.lexsort((np.arange(E), -x[m]))[:K] for m in range(M)])
+        assert (ids[:, :K] == top).all()
+        wr = np.take_along_axis(sm, top, 1)
+        if rn:
+            wr = wr / wr.sum(1, keepdims=True)
+        close(w[:, :K], wr, what="shared-gate routed")
+        close(w[:, K:K + S], sc * scipy.special.expit(hs @ gw.T), rtol=1e-12, atol=1e-15,
+              what="shared gates")
+        assert (ids[:, K:K + S] == 1000 + np.arange(S)).all()
+        assert np.isnan(w[:, K + S:]).all() and (ids[:, K + S:] == -1).all()
+
+
+def pin_shared_gate_invariants(lib):
+    """The routed columns equal the decode routing oracle's softmax slots;
+    the gates scale linearly with `scale`, ignore the gating logits, and
+    swap with the gate-weight rows."""
+    rng = np.random.default_rng(32)
+    x = rng.normal(0, 2, (6, 128))
+    hs = rng.normal(0, 1, (6, 33))
+    gw = rng.normal(0, 0.3, (4, 33))
+    w, ids = oracle.topk_shared_gate(x, hs, gw, 7, True, 1.0, 128, lib=lib)
+    r = oracle.route_maps(x, 7, oracle.SOFTMAX, True, lib=lib)
+    assert (ids[:, :7] == r["ids"]).all()
+    close(w[:, :7], r["weights"], what="routed vs route maps")
+    w2, _ = oracle.topk_shared_gate(-x, hs, gw, 7, True, 3.0, 128, lib=lib)
+    close(w2[:, 7:], 3.0 * w[:, 7:], what="scale / gating independence")
+    w3, _ = oracle.topk_shared_gate(x, hs, gw[::-1].copy(), 7, True, 1.0, 128, lib=lib)
+    close(w3[:, 7:], w[:, 7:][:, ::-1], what="gate rows")
+
+
 PINS = [pin_golden, pin_score_library, pin_topk_bruteforce,
         pin_groups_bruteforce, pin_renorm_identities, pin_scale_linearity,
         pin_backward_fd, pin_aux_backward_fd, pin_backward_invariants,
         pin_rows_independent, pin_margin, pin_tokens_per_expert,
         pin_aux_loss_closed_forms, pin_aux_loss_fd, pin_route_maps_bruteforce,
-        pin_route_maps_vs_topk]
+        pin_route_maps_vs_topk, pin_shared_gate_library, pin_shared_gate_invariants]

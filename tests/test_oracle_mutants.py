@@ -90,6 +90,17 @@ MUTANTS = [
      "unperm_to_perm[p] = pairs[p].unpermuted;", 0),
     ("maps_ids_unsorted_slot", "ids[t * K + k] = work[k].idx;",
      "ids[t * K + k] = work[K - 1 - k].idx;", 0),
+    ("gate_sign", "weights[m * ld + K + s] = scale / (1.0 + exp(-dot));",
+     "weights[m * ld + K + s] = scale / (1.0 + exp(dot));", 0),
+    ("gate_scale_dropped", "weights[m * ld + K + s] = scale / (1.0 + exp(-dot));",
+     "weights[m * ld + K + s] = 1.0 / (1.0 + exp(-dot));", 0),
+    ("gate_weight_row", "dot += hs[m * H + h] * gw[(int64_t)s * H + h];",
+     "dot += hs[m * H + h] * gw[h];", 0),
+    ("gate_hidden_row", "dot += hs[m * H + h] * gw[(int64_t)s * H + h];",
+     "dot += hs[h] * gw[(int64_t)s * H + h];", 0),
+    ("gate_id_base", "ids[m * ld + K + s] = shared_base + s;",
+     "ids[m * ld + K + s] = shared_base + s + 1;", 0),
+    ("gate_routed_not_renormed", "denom += sc[work[k].idx];", "denom += sc[work[0].idx];", 0),
     ("margin_sign", "gap = work[K - 1].key - work[K].key;",
      "gap = work[K].key - work[K - 1].key;", 0),
 ]

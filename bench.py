@@ -257,6 +257,51 @@ def run_configs(torch, router, synth, np, steps):
     return out
 
 
+# Fused shared-gate op of the aiter page on gfx950 (MI35X), microseconds per
+# call at E=512, H=4096, top-10, one shared expert, bf16 (context only: its
+# own table, "PROVISIONAL - single run").
+PAGE_AITER_FUSED_US = {1: 14.6, 4: 13.9, 16: 15.2, 64: 14.8, 256: 15.8, 1024: 16.6,
+                       4096: 23.5, 16384: 44.2}
+
+
+def shared_gate_bytes(M, E=512, H=4096, K=10, S=1, esz=2):
+    """Algorithmic bytes: gating and hidden rows read once, gate weights
+    read once, K+S weights and ids written per token."""
+    return M * E * esz + M * H * esz + S * H * esz + M * (K + S) * 8
+
+
+def run_shared_gate(torch, router, synth, steps):
+    """Routed top-k with the shared-expert gate at the aiter page's shape
+    (E=512 experts, hidden 4096, top-10, one shared expert, bf16) over its
+    token sweep; calls replayed from a HIP graph; from M=1024 on the inputs
+    rotate over >= 2 GiB of buffer sets (cold caches)."""
+    dev = torch.device("cuda:0")
+    E, H, K, S = 512, 4096, 10, 1
+    out = {}
+    for M in (1, 4, 16, 64, 256, 1024, 4096, 16384):
+        def dev_bf16(seed, shape, std):
+            bits = synth.storage(synth.normal(seed, shape, std), synth.BF16)[0]
+            return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
+        x0 = dev_bf16(9700 + M, (M, E), 1.0)
+        h0 = dev_bf16(9701 + M, (M, H), 1.0)
+        g = dev_bf16(9702, (S, H), 0.05)
+        per = M * (E + H) * 2
+        n = max(1, -(-(2 << 30) // per)) if M >= 1024 else 1
+        sets = [(x0.clone(), h0.clone()) for _ in range(n)] if n > 1 else [(x0, h0)]
+        w = torch.empty((M, K + S), dtype=torch.float32, device=dev)
+        ids = torch.empty((M, K + S), dtype=torch.int32, device=dev)
+        calls = [lambda st=sets[i % len(sets)]: router.router_topk_shared_gate(
+            st[0], st[1], g, K, True, 1.0, E, out=(w, ids)) for i in range(steps)]
+        us = graph_us_per_launch(torch, calls)
+        nb = shared_gate_bytes(M, E, H, K, S)
+        out[f"M{M}"] = {"us_graph": round(us, 2), "GBps": round(nb / us / 1e3, 1),
+                        "frac_of_peak": round(nb / us / 1e3 / PEAK_GBPS, 4),
+                        "algo_bytes": nb, "cold": n > 1,
+                        "page_aiter_fused_us_context": PAGE_AITER_FUSED_US[M]}
+        del sets, x0, h0
+    return out
+
+
 def run_decode_route(torch, router, synth, steps):
     """Latency of decode-shape routing with expert maps (one workgroup per
     call) at the onnxruntime page's shapes: T in 1..4 rows, E = 512 experts,
@@ -305,6 +350,8 @@ def main():
                     help="time only this kernel kind (for profiler runs)")
     ap.add_argument("--only-decode-route", action="store_true",
                     help="time only the decode routing (for profiler runs)")
+    ap.add_argument("--only-shared-gate", action="store_true",
+                    help="time only the shared-gate sweep (for profiler runs)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the T=8192 E/K sweep object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -323,6 +370,11 @@ def main():
     if args.only_decode_route:
         torch.cuda.set_device(0)
         print(json.dumps({"decode_route": run_decode_route(torch, router, synth, args.steps)}),
+              flush=True)
+        return
+    if args.only_shared_gate:
+        torch.cuda.set_device(0)
+        print(json.dumps({"shared_gate": run_shared_gate(torch, router, synth, args.steps)}),
               flush=True)
         return
 
@@ -553,6 +605,11 @@ def main():
         out["decode_route_note"] = (
             "decode-shape routing with expert maps (one workgroup): microseconds per call, "
             "T rows x E=512 experts x K, softmax renormalised, fp32")
+        out["shared_gate"] = run_shared_gate(torch, router, synth, max(10, args.steps // 4))
+        out["shared_gate_note"] = (
+            "routed softmax top-k with the shared-expert sigmoid gate: M tokens x E=512 x "
+            "hidden 4096, top-10, one shared expert, bf16, renormalised; graph-replayed; "
+            "GB/s = gating + hidden + gate rows read, weights and ids written")
     if not args.no_sweep and not args.only:
         out["configs"] = run_configs(torch, router, synth, np, max(10, args.steps // 4))
         out["configs_note"] = ("the five router workloads (c1..c5), cold, launches replayed "

@@ -7,10 +7,12 @@
  * fused_score_for_moe_aux_loss, each with a forward and a backward, as
  * hand-written HIP kernels; the load-balancing loss that consumes the aux
  * scores (the page's fused_moe_aux_loss, "Files changed"), with the
- * tokens-per-expert counts it needs; and decode-shape routing with the
+ * tokens-per-expert counts it needs; decode-shape routing with the
  * (expert, token)-sorted expert maps of "[CUDA] Add fused decode routing,
  * single-pass finalize, and PDL overlap for NVFP4 QMoE" (onnxruntime pull
- * request 33366).
+ * request 33366); and the routed top-k with the shared-expert sigmoid gate
+ * of "[HIP] [Perf] Fold shared-expert gate GEMV into topk_softmax kernel"
+ * (ROCm aiter pull request 5652).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -257,6 +259,42 @@ router_status router_route_maps(const void *logits, int dtype, int32_t T,
                                 int32_t *perm_to_unperm,
                                 int32_t *unperm_to_perm, int32_t *perm_expert,
                                 int64_t *expert_offsets, void *hip_stream);
+
+/*
+ * router_topk_shared_gate -- routed softmax top-k with the shared-expert
+ * sigmoid gate in the same kernel.  Passage: the aiter fused-gate page
+ * (the op topk_softmax_fused_shared_gate: hidden_states, gate_weight,
+ * shared_expert_scale, shared_expert_base; the unfused baseline of its
+ * review: topk_softmax, then sigmoid(hidden_states @ gate_weight^T) *
+ * scale into the columns after top_k, shared ids base + s).
+ *
+ * Per token m: slots k < K hold the K largest gating logits in descending
+ * order (ties: lower expert): topk_ids[m*ld + k] = expert,
+ * topk_weights[m*ld + k] = softmax score, divided by the sum of the K
+ * selected scores when renorm.  Slots K + s, s < S:
+ *   topk_weights[m*ld + K + s] = shared_scale * sigmoid(sum_h
+ *       hidden[m,h] * gate_weight[s,h]),  topk_ids = shared_base + s.
+ * gating [M,E], hidden [M,H] and gate_weight [S,H] are row-major in
+ * `dtype`; the dot products accumulate in fp32.  Output rows have stride
+ * ld >= K + S (elements); columns past K + S are not touched.
+ * Limits: E <= ROUTER_GATE_MAX_EXPERTS, K <= ROUTER_GATE_MAX_K,
+ * S <= ROUTER_GATE_MAX_SHARED (else UNSUPPORTED); any H >= 1 (16-byte
+ * aligned rows with H a multiple of 8 bf16 / 4 fp32 elements take vector
+ * loads).  M == 0 is a no-op.  Errors (INVALID_ARG): dtype, E, H, K
+ * outside [1, E], S < 1, ld < K + S, non-finite scale, shared_base < 0 or
+ * shared_base + S past INT32_MAX, null or misaligned pointers; OVERFLOW
+ * when S*H elements or M rows overflow the offsets.
+ */
+#define ROUTER_GATE_MAX_EXPERTS 1024
+#define ROUTER_GATE_MAX_K 32
+#define ROUTER_GATE_MAX_SHARED 16
+router_status router_topk_shared_gate(const void *gating, const void *hidden,
+                                      const void *gate_weight, int dtype,
+                                      int64_t M, int32_t E, int32_t H, int32_t K,
+                                      int32_t S, int renorm, float shared_scale,
+                                      int32_t shared_base, float *topk_weights,
+                                      int32_t *topk_ids, int64_t ld,
+                                      void *hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char *router_status_str(router_status s);

@@ -478,6 +478,55 @@ router_status router_route_maps(const void *logits, int dtype, int32_t T, int32_
                : ROUTER_ERR_HIP;
 }
 
+router_status router_topk_shared_gate(const void *gating, const void *hidden,
+                                      const void *gate_weight, int dtype, int64_t M, int32_t E,
+                                      int32_t H, int32_t K, int32_t S, int renorm,
+                                      float shared_scale, int32_t shared_base,
+                                      float *topk_weights, int32_t *topk_ids, int64_t ld,
+                                      void *hip_stream)
+{
+    if (dtype != ROUTER_F32 && dtype != ROUTER_BF16)
+        return ROUTER_ERR_INVALID_ARG;
+    if (M < 0 || E < 1 || H < 1 || K < 1 || K > E || S < 1 || ld < (int64_t)K + S)
+        return ROUTER_ERR_INVALID_ARG;
+    if (!std::isfinite(shared_scale) || shared_base < 0 || shared_base > INT32_MAX - S)
+        return ROUTER_ERR_INVALID_ARG;
+    if (E > ROUTER_GATE_MAX_EXPERTS || K > ROUTER_GATE_MAX_K || S > ROUTER_GATE_MAX_SHARED)
+        return ROUTER_ERR_UNSUPPORTED;
+    const size_t ds = dsize(dtype);
+    if ((int64_t)S * H * (int64_t)ds > INT32_MAX || M > INT64_MAX / ((int64_t)H * 4) ||
+        M > INT64_MAX / ((int64_t)E * 4) || M > INT64_MAX / (ld * 4))
+        return ROUTER_ERR_OVERFLOW;
+    if (M == 0)
+        return ROUTER_OK;
+    if (!gating || !hidden || !gate_weight || !topk_weights || !topk_ids)
+        return ROUTER_ERR_INVALID_ARG;
+    if (!aligned(gating, ds) || !aligned(hidden, ds) || !aligned(gate_weight, ds) ||
+        !aligned(topk_weights, 4) || !aligned(topk_ids, 4))
+        return ROUTER_ERR_INVALID_ARG;
+    GateParams p{};
+    p.x = gating;
+    p.hs = hidden;
+    p.gw = gate_weight;
+    p.weights = topk_weights;
+    p.ids = topk_ids;
+    p.M = M;
+    p.ld = ld;
+    p.E = E;
+    p.H = H;
+    p.K = K;
+    p.S = S;
+    p.renorm = renorm ? 1 : 0;
+    p.base = shared_base;
+    p.scale = shared_scale;
+    const bool vec_g = E % 4 == 0 && aligned(gating, 4 * ds);
+    const int vh = (int)(16 / ds);
+    const bool vec_h = H % vh == 0 && aligned(hidden, 16) && aligned(gate_weight, 16);
+    return launch_shared_gate(p, dtype, vec_g, vec_h, (hipStream_t)hip_stream) == hipSuccess
+               ? ROUTER_OK
+               : ROUTER_ERR_HIP;
+}
+
 const char *router_status_str(router_status s)
 {
     switch (s) {

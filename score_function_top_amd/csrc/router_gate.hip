@@ -1,0 +1,178 @@
+// router_gate.hip -- routed softmax top-k with the shared-expert sigmoid gate
+// folded into the same kernel, on gfx950.
+//
+// Operation: "[HIP] [Perf] Fold shared-expert gate GEMV into topk_softmax
+// kernel" (ROCm aiter pull request 5652): per token the routed top-k slots
+// of the softmax over the gating logits, and for each shared expert s the
+// gate scale * sigmoid(hidden_states[m,:] . gate_weight[s,:]) with id
+// shared_base + s in the columns after the K routed ones.  The maths is
+// stated in include/router.h.
+//
+// One wave per token (grid-stride over tokens).  The routed half is the
+// ordered top-K of router_topk_wave.h.  The gate half is a GEMV with S <= 16
+// outputs per token, bound by the hidden-state read (H elements per token,
+// S flops each): it runs on the VALU, not on matrix cores.  Lane l owns
+// the 16-byte pieces h = c*64*VH + VH*l (VH elements per piece); each piece
+// of the hidden row is read once (non-temporal) and dotted with the same
+// piece of every gate row (shared by all tokens, so it stays in the caches;
+// bf16 pairs through v_dot2_f32_bf16, whose products are exact in fp32),
+// then S wave sums give the gate logits.
+#include <hip/hip_runtime.h>
+
+#include "router_io.h"
+#include "router_params.h"
+#include "router_topk_wave.h"
+
+namespace rker {
+
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename TIn>
+__device__ __forceinline__ float dot16(const uint32_t (&a)[4], const uint32_t (&b)[4], float acc)
+{
+    if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[q]),
+                                                  __builtin_bit_cast(bf16x2_t, b[q]), acc, false);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            acc = fmaf(as_f(a[q]), as_f(b[q]), acc);
+    }
+    return acc;
+}
+
+// 16 bytes of a row at element offset h (elements past H read as 0).
+template <typename TIn, bool VEC, int POL>
+__device__ __forceinline__ void load16(rsrc_t r, int h, int H, uint32_t (&v)[4])
+{
+    constexpr int VH = 16 / (int)sizeof(TIn);
+    constexpr uint32_t sz = (uint32_t)sizeof(TIn);
+    if constexpr (VEC) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(
+            r, (int)(h < H ? (uint32_t)h * sz : kOOB), 0, POL);
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            v[q] = t[q];
+    } else if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int h0 = h + 2 * q;
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                r, (int)(h0 < H ? (uint32_t)h0 * sz : kOOB), 0, POL);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                r, (int)(h0 + 1 < H ? (uint32_t)(h0 + 1) * sz : kOOB), 0, POL);
+            v[q] = (lo & 0xFFFFu) | (hi << 16);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < VH; q++)
+            v[q] = __builtin_amdgcn_raw_buffer_load_b32(
+                r, (int)(h + q < H ? (uint32_t)(h + q) * sz : kOOB), 0, POL);
+    }
+}
+
+template <int NCH, typename TIn, bool VEC_G, bool VEC_H>
+__global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
+{
+    constexpr uint32_t sz = io<TIn>::kSize;
+    constexpr int VH = 16 / (int)sz;  // hidden elements per 16-byte piece
+    const int lane = lane_id();
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int E = p.E, H = p.H, K = p.K, S = p.S;
+    const int pieces = (H + 64 * VH - 1) / (64 * VH);
+    const rsrc_t rgw = make_rsrc(p.gw, (uint32_t)S * (uint32_t)H * sz);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+
+    for (int64_t m = (int64_t)blockIdx.x * kWaves + wave; m < p.M; m += nwaves) {
+        // routed half
+        const rsrc_t rx = make_rsrc((const char *)p.x + m * E * sz, (uint32_t)E * sz);
+        int id;
+        float wt;
+        wave_topk_row<NCH, TIn, VEC_G>(rx, E, K, SCORE_SOFTMAX, p.renorm, id, wt);
+
+        // gate half: S dot products over the hidden row
+        const rsrc_t rh = make_rsrc((const char *)p.hs + m * H * sz, (uint32_t)H * sz);
+        float acc[kGateMaxShared];
+#pragma unroll
+        for (int s = 0; s < kGateMaxShared; s++)
+            acc[s] = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < pieces; c++) {
+            const int h = c * 64 * VH + VH * lane;
+            uint32_t hv[4];
+            load16<TIn, VEC_H, kStream>(rh, h, H, hv);
+#pragma unroll
+            for (int s = 0; s < kGateMaxShared; s++) {
+                if (s < S) {
+                    uint32_t gv[4];
+                    load16<TIn, VEC_H, 0>(rgw, s * H + h, s * H + H, gv);
+                    acc[s] = dot16<TIn>(hv, gv, acc[s]);
+                }
+            }
+        }
+        float gate = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kGateMaxShared; s++) {
+            if (s < S) {
+                const float logit = group_sum<64>(acc[s]);
+                gate = lane == K + s ? p.scale * sigmoid_fast(logit) : gate;
+            }
+        }
+
+        // row m of the outputs: K routed slots, then S gates
+        const uint32_t nb = (uint32_t)(K + S) * 4u;
+        const rsrc_t rw = make_rsrc(p.weights + m * p.ld, nb);
+        const rsrc_t ri = make_rsrc(p.ids + m * p.ld, nb);
+        const bool routed = lane < K;
+        const bool shared = lane >= K && lane < K + S;
+        const uint32_t o = routed || shared ? (uint32_t)lane * 4u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b32(as_u(routed ? wt : gate), rw, (int)o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            (uint32_t)(routed ? id : p.base + (lane - K)), ri, (int)o, 0, 0);
+    }
+}
+
+template <int NCH, typename TIn>
+hipError_t gate_t(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hipStream_t st)
+{
+    const dim3 g(grid), b(kBlock);
+    if (vec_g && vec_h)
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, true>), g, b, 0, st, p);
+    else if (vec_g)
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, false>), g, b, 0, st, p);
+    else if (vec_h)
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, true>), g, b, 0, st, p);
+    else
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, false>), g, b, 0, st, p);
+    return hipGetLastError();
+}
+
+template <int NCH>
+hipError_t gate_nch(const GateParams &p, int dtype, bool vec_g, bool vec_h, unsigned grid,
+                    hipStream_t st)
+{
+    return dtype == 0 ? gate_t<NCH, float>(p, vec_g, vec_h, grid, st)
+                      : gate_t<NCH, uint16_t>(p, vec_g, vec_h, grid, st);
+}
+
+}  // namespace
+
+hipError_t launch_shared_gate(const GateParams &p, int dtype, bool vec_g, bool vec_h,
+                              hipStream_t stream)
+{
+    if (p.M == 0)
+        return hipSuccess;
+    const int64_t blocks = (p.M + kWaves - 1) / kWaves;
+    const unsigned grid = (unsigned)(blocks < kGateMaxBlocks ? blocks : kGateMaxBlocks);
+    if (p.E <= 256)
+        return gate_nch<1>(p, dtype, vec_g, vec_h, grid, stream);
+    if (p.E <= 512)
+        return gate_nch<2>(p, dtype, vec_g, vec_h, grid, stream);
+    return gate_nch<4>(p, dtype, vec_g, vec_h, grid, stream);
+}
+
+}  // namespace rker

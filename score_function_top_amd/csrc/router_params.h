@@ -189,6 +189,30 @@ struct RouteParams {
 
 hipError_t launch_route_maps(const RouteParams &p, int dtype, bool vec, hipStream_t stream);
 
+// Routed top-k with the shared-expert gate (one wave per token).
+constexpr int kGateMaxShared = 16;
+constexpr int kGateMaxBlocks = 65536;  // the kernel strides over further tokens
+
+struct GateParams {
+    const void *x;      // gating logits [M,E]
+    const void *hs;     // hidden states [M,H]
+    const void *gw;     // gate weights [S,H]
+    float *weights;     // [M, ld]
+    int32_t *ids;       // [M, ld]
+    int64_t M;
+    int64_t ld;
+    int E;
+    int H;
+    int K;
+    int S;
+    int renorm;
+    int base;
+    float scale;
+};
+
+hipError_t launch_shared_gate(const GateParams &p, int dtype, bool vec_g, bool vec_h,
+                              hipStream_t stream);
+
 // Chunk counts built per lane-group width (see router_launch.h).
 constexpr int kNchLpt16[] = {1, 2, 4};
 constexpr int kNchLpt32[] = {1, 2, 4};

@@ -12,10 +12,8 @@
 // first permuted row of each expert).  The maths is stated in
 // include/router.h.
 //
-// One wave per token (T <= 16 waves in the block).  Lane l holds elements
-// j = c*256 + 4*l + u.  Slot k is the k-th round of a wave-wide maximum of
-// the packed key ord(x) << 32 | ~j (larger logit first, ties to the lower
-// index); lane k keeps slot k.  The maps need no sort: each expert's LDS
+// One wave per token (T <= 16 waves in the block) runs the ordered top-K of
+// router_topk_wave.h; lane k keeps slot k.  The maps need no sort: each expert's LDS
 // word collects a bit per token that chose it, so the expert offsets are an
 // exclusive scan of the words' popcounts and pair (t, k) -> expert e lands
 // at offset[e] + popcount(word[e] & ((1 << t) - 1)), which is the
@@ -24,17 +22,13 @@
 
 #include "router_io.h"
 #include "router_params.h"
+#include "router_topk_wave.h"
 
 namespace rker {
 
 namespace {
 
 constexpr int kRouteMaxPairs = kRouteMaxRows * kRouteMaxK;
-
-__device__ __forceinline__ uint64_t route_key(float x, uint32_t j)
-{
-    return ((uint64_t)ord_key(x + 0.0f) << 32) | (uint32_t)~j;
-}
 
 template <int NCH, typename TIn, bool VEC>
 __global__ __launch_bounds__(kRouteMaxRows * 64) void route_maps_kernel(RouteParams p)
@@ -57,93 +51,9 @@ __global__ __launch_bounds__(kRouteMaxRows * 64) void route_maps_kernel(RoutePar
     if (w < T) {
         constexpr uint32_t sz = io<TIn>::kSize;
         const rsrc_t r = make_rsrc((const char *)p.x + (int64_t)w * E * sz, (uint32_t)E * sz);
-        float key[NCH][4];
-#pragma unroll
-        for (int c = 0; c < NCH; c++) {
-            const int j0 = c * 256 + 4 * lane;
-            if constexpr (VEC) {
-                io<TIn>::load4(r, j0 < E ? (uint32_t)j0 * sz : kOOB, 0, key[c]);
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    key[c][u] = j0 < E ? key[c][u] : -INFINITY;
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    const bool ok = j0 + u < E;
-                    const float v = io<TIn>::load1(r, ok ? (uint32_t)(j0 + u) * sz : kOOB);
-                    key[c][u] = ok ? v : -INFINITY;
-                }
-            }
-        }
-        float mx = 0.0f, rz = 0.0f;
-        if (p.score == SCORE_SOFTMAX) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int c = 0; c < NCH; c++)
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    m = fmaxf(m, key[c][u]);
-            mx = group_max<64>(m);
-            float z = 0.0f;
-#pragma unroll
-            for (int c = 0; c < NCH; c++)
-#pragma unroll
-                for (int u = 0; u < 4; u++)
-                    z += exp_split(key[c][u] - mx);  // padding: exactly 0
-            rz = 1.0f / group_sum<64>(z);
-        }
-        // the lane's packed keys, sorted descending once (bitonic network);
-        // padding packs to 0, below every real key
-        constexpr int V = NCH * 4;
-        uint64_t lst[V];
-#pragma unroll
-        for (int c = 0; c < NCH; c++)
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                lst[c * 4 + u] = key[c][u] == -INFINITY
-                                     ? 0ull
-                                     : route_key(key[c][u], (uint32_t)(c * 256 + 4 * lane + u));
-#pragma unroll
-        for (int k2 = 2; k2 <= V; k2 <<= 1)
-#pragma unroll
-            for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1)
-#pragma unroll
-                for (int i = 0; i < V; i++) {
-                    const int l2 = i ^ j2;
-                    if (l2 > i) {
-                        // descending where bit k2 of i is clear, ascending where set
-                        const bool desc = (i & k2) == 0;
-                        const uint64_t a = lst[i], b = lst[l2];
-                        const bool swap = desc ? (b > a) : (a > b);
-                        lst[i] = swap ? b : a;
-                        lst[l2] = swap ? a : b;
-                    }
-                }
-        // K ordered rounds: the wave maximum of the lanes' heads; the
-        // winning lane pops its head; lane k keeps slot k
-        int my_id = 0;
-        float my_s = 0.0f;
-        for (int k = 0; k < K; k++) {
-            const uint64_t best = group_max_u64<64>(lst[0]);
-            const bool win = lst[0] == best;
-#pragma unroll
-            for (int i = 0; i + 1 < V; i++)
-                lst[i] = win ? lst[i + 1] : lst[i];
-            lst[V - 1] = win ? 0ull : lst[V - 1];
-            const uint32_t jw = ~(uint32_t)best;
-            const float xw = ord_key_inv((uint32_t)(best >> 32));
-            const float sw = p.score == SCORE_SOFTMAX ? exp_split(xw - mx) * rz : sigmoid_fast(xw);
-            my_id = lane == k ? (int)jw : my_id;
-            my_s = lane == k ? sw : my_s;
-        }
-        float wgt = my_s;
-        if (p.renorm && (p.score == SCORE_SOFTMAX || K > 1)) {
-            // the selected scores in slot order, summed sequentially
-            float den = 0.0f;
-            for (int k = 0; k < K; k++)
-                den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
-            wgt = my_s / den;
-        }
+        int my_id;
+        float wgt;
+        wave_topk_row<NCH, TIn, VEC>(r, E, K, p.score, p.renorm, my_id, wgt);
         if (lane < K) {
             const rsrc_t rw = make_rsrc(p.weights, (uint32_t)n * 4u);
             const rsrc_t ri = make_rsrc(p.ids, (uint32_t)n * 4u);

@@ -9,7 +9,7 @@ fallback: if librouter.so is not built, every call raises.
 Entry points carry the C names: router_topk_fwd, router_topk_bwd,
 router_aux_scores, router_aux_scores_bwd, router_tokens_per_expert,
 router_aux_loss_fwd, router_aux_loss_bwd, router_aux_loss_workspace_bytes,
-router_route_maps.
+router_route_maps, router_topk_shared_gate.
 """
 import ctypes
 import os
@@ -24,6 +24,7 @@ F32, BF16 = 0, 1
 SOFTMAX, SIGMOID = 0, 1
 MAX_EXPERTS = 4096
 ROUTE_MAX_ROWS, ROUTE_MAX_EXPERTS, ROUTE_MAX_K = 16, 1024, 32
+GATE_MAX_EXPERTS, GATE_MAX_K, GATE_MAX_SHARED = 1024, 32, 16
 
 _SCORE = {"softmax": SOFTMAX, "sigmoid": SIGMOID, SOFTMAX: SOFTMAX,
           SIGMOID: SIGMOID}
@@ -64,6 +65,9 @@ def load():
     lib.router_aux_loss_bwd.argtypes = [vp, vp, ci, i64, i32, i64, i32, f32, vp, vp]
     lib.router_route_maps.argtypes = [vp, ci, i32, i32, i32, ci, ci, vp, vp, vp, vp, vp, vp, vp]
     lib.router_route_maps.restype = ci
+    lib.router_topk_shared_gate.argtypes = [vp, vp, vp, ci, i64, i32, i32, i32, i32, ci, f32,
+                                            i32, vp, vp, i64, vp]
+    lib.router_topk_shared_gate.restype = ci
     for f in (lib.router_topk_fwd, lib.router_topk_bwd, lib.router_aux_scores,
               lib.router_aux_scores_bwd, lib.router_set_topk_path_threshold,
               lib.router_tokens_per_expert, lib.router_aux_loss_fwd, lib.router_aux_loss_bwd):
@@ -290,3 +294,37 @@ def router_route_maps(logits, topk, score_function="softmax", renorm=False, out=
         _ptr(res["perm_to_unperm"]), _ptr(res["unperm_to_perm"]), _ptr(res["perm_expert"]),
         _ptr(res["expert_offsets"]), _stream(logits)))
     return res
+
+
+def router_topk_shared_gate(gating, hidden, gate_weight, topk, renorm=True, shared_scale=1.0,
+                            shared_base=None, out=None):
+    """Routed softmax top-k plus shared-expert sigmoid gates.  gating [M,E],
+    hidden [M,H], gate_weight [S,H] (one dtype, float32 or bfloat16).
+    Returns (weights [M, K+S] float32, ids [M, K+S] int32); `out` may pass
+    that pair preallocated, also as column views of wider rows (row stride
+    taken from the tensors, unit column stride)."""
+    M, E = _rows(gating, "gating")
+    Mh, H = _rows(hidden, "hidden")
+    S, Hw = _rows(gate_weight, "gate_weight")
+    if Mh != M or Hw != H or hidden.dtype != gating.dtype or gate_weight.dtype != gating.dtype:
+        raise ValueError("hidden must be [M,H] and gate_weight [S,H], all in the gating dtype")
+    K = int(topk)
+    dev = gating.device
+    base = E if shared_base is None else int(shared_base)
+    if out is None:
+        w = torch.empty((M, K + S), dtype=torch.float32, device=dev)
+        ids = torch.empty((M, K + S), dtype=torch.int32, device=dev)
+    else:
+        w, ids = out
+        for t, dt, name in ((w, torch.float32, "weights"), (ids, torch.int32, "ids")):
+            if (t.dtype != dt or t.device != dev or t.dim() != 2 or t.shape != (M, K + S)
+                    or (M > 1 and t.stride(1) != 1)):
+                raise ValueError(f"{name} must be a {dt} [{M}, {K + S}] tensor with unit "
+                                 f"column stride on {dev}")
+        if w.stride(0) != ids.stride(0):
+            raise ValueError("weights and ids must share one row stride")
+    ld = w.stride(0) if M > 1 else K + S
+    check(load().router_topk_shared_gate(
+        _ptr(gating), _ptr(hidden), _ptr(gate_weight), _DTYPE[gating.dtype], M, E, H, K, S,
+        int(bool(renorm)), float(shared_scale), base, _ptr(w), _ptr(ids), ld, _stream(gating)))
+    return w, ids

@@ -226,3 +226,23 @@ def test_route_maps_host_checks():
                    (dict(off=None), INV), (dict(off=P + 4), INV), (dict(x=P + 2), INV),
                    (dict(dtype=1, x=P + 1), INV), (dict(ids=P + 2), INV)):
         assert call(**kw) == st, kw
+
+
+def test_shared_gate_host_checks():
+    f = router.load().router_topk_shared_gate
+
+    def call(**kw):
+        a = dict(x=P, h=P, g=P, dtype=1, M=8, E=512, H=4096, K=10, S=1, renorm=1, scale=1.0,
+                 base=512, w=P, ids=P, ld=11)
+        a.update(kw)
+        return f(a["x"], a["h"], a["g"], a["dtype"], a["M"], a["E"], a["H"], a["K"], a["S"],
+                 a["renorm"], a["scale"], a["base"], a["w"], a["ids"], a["ld"], None)
+    for kw, st in ((dict(dtype=5), INV), (dict(M=-1), INV), (dict(E=0), INV), (dict(H=0), INV),
+                   (dict(K=0), INV), (dict(K=513), INV), (dict(S=0), INV), (dict(ld=10), INV),
+                   (dict(scale=float("nan")), INV), (dict(base=-1), INV),
+                   (dict(base=2 ** 31 - 1), INV), (dict(E=1025), UNS), (dict(K=33, ld=34), UNS),
+                   (dict(S=17, ld=27), UNS), (dict(x=None), INV), (dict(h=None), INV),
+                   (dict(g=None), INV), (dict(w=None), INV), (dict(ids=None), INV),
+                   (dict(x=P + 1), INV), (dict(w=P + 2), INV),
+                   (dict(M=2 ** 61), OVF), (dict(M=0), OK), (dict(M=0, x=None, w=None), OK)):
+        assert call(**kw) == st, kw

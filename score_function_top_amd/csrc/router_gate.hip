@@ -78,6 +78,7 @@ __device__ __forceinline__ void load16(rsrc_t r, int h, int H, uint32_t (&v)[4])
 template <int NCH, typename TIn, bool VEC_G, bool VEC_H>
 __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
 {
+    __shared__ uint64_t cand[kWaves][kSortedSlots];
     constexpr uint32_t sz = io<TIn>::kSize;
     constexpr int VH = 16 / (int)sz;  // hidden elements per 16-byte piece
     const int lane = lane_id();
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
         const rsrc_t rx = make_rsrc((const char *)p.x + m * E * sz, (uint32_t)E * sz);
         int id;
         float wt;
-        wave_topk_row<NCH, TIn, VEC_G>(rx, E, K, SCORE_SOFTMAX, p.renorm, id, wt);
+        wave_topk_row<NCH, TIn, VEC_G>(rx, E, K, SCORE_SOFTMAX, p.renorm, cand[wave], id, wt);
 
         // gate half: S dot products over the hidden row
         const rsrc_t rh = make_rsrc((const char *)p.hs + m * H * sz, (uint32_t)H * sz);

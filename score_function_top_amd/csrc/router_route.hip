@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kRouteMaxRows * 64) void route_maps_kernel(RoutePar
     __shared__ uint32_t offs[kRouteMaxExperts + 1];
     __shared__ int32_t pair_expert[kRouteMaxPairs];  // by unpermuted index t + k*T
     __shared__ uint32_t wave_tot[kRouteMaxRows];
+    __shared__ uint64_t cand[kRouteMaxRows][kSortedSlots];
 
     const int T = p.T, E = p.E, K = p.K, n = T * K;
     const int nthreads = (int)blockDim.x;
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kRouteMaxRows * 64) void route_maps_kernel(RoutePar
         const rsrc_t r = make_rsrc((const char *)p.x + (int64_t)w * E * sz, (uint32_t)E * sz);
         int my_id;
         float wgt;
-        wave_topk_row<NCH, TIn, VEC>(r, E, K, p.score, p.renorm, my_id, wgt);
+        wave_topk_row<NCH, TIn, VEC>(r, E, K, p.score, p.renorm, cand[w], my_id, wgt);
         if (lane < K) {
             const rsrc_t rw = make_rsrc(p.weights, (uint32_t)n * 4u);
             const rsrc_t ri = make_rsrc(p.ids, (uint32_t)n * 4u);

@@ -20,8 +20,10 @@ from score_function_top_amd import router, synth
 pytestmark = pytest.mark.gpu
 
 
-def inputs(seed, M, E, H, S, dtype, views=False):
+def inputs(seed, M, E, H, S, dtype, views=False, ties=False):
     x_st, x64 = synth.storage(synth.normal(seed, (M, E), 1.0), dtype)
+    if ties:   # small integers: many keys tie at the pruning bound
+        x_st, x64 = synth.storage(np.round(synth.normal(seed, (M, E), 1.0)), dtype)
     h_st, h64 = synth.storage(synth.normal(seed + 1, (M, H), 1.0), dtype)
     g_st, g64 = synth.storage(synth.normal(seed + 2, (S, H), 0.05), dtype)
     if views:
@@ -35,11 +37,11 @@ def inputs(seed, M, E, H, S, dtype, views=False):
 
 
 def run(M, E, H, K, S, dtype=synth.BF16, renorm=True, scale=1.0, base=None, ld_extra=0,
-        views=False, seed=None):
+        views=False, seed=None, ties=False):
     seed = seed if seed is not None else 9500 + M + E + H + K + S
     say(f"[shared gate] M={M} E={E} H={H} K={K} S={S} dtype={dtype} renorm={renorm} "
         f"scale={scale} ld+{ld_extra} views={views}")
-    (xt, ht, gt), (x64, h64, g64) = inputs(seed, M, E, H, S, dtype, views)
+    (xt, ht, gt), (x64, h64, g64) = inputs(seed, M, E, H, S, dtype, views, ties)
     out = None
     if ld_extra:
         wbig = torch.full((M, K + S + ld_extra), -7.0, dtype=torch.float32, device=DEV)
@@ -72,7 +74,8 @@ def test_page_shape(M):
     dict(E=256), dict(M=65), dict(M=1, S=8, dtype=synth.F32), dict(base=0),
     dict(E=160, K=7), dict(E=1000, K=32, S=16), dict(E=1, K=1), dict(H=4100),
     dict(H=33, dtype=synth.F32), dict(H=7168), dict(ld_extra=5), dict(views=True),
-    dict(views=True, dtype=synth.F32, H=100),
+    dict(views=True, dtype=synth.F32, H=100), dict(ties=True), dict(ties=True, K=32),
+    dict(K=3), dict(K=4),
 ])
 def test_page_axes_and_edges(kw):
     """The page's test axes (S = 2 and 8, fp32 inputs, no renorm, scale 0.5,

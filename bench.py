@@ -66,9 +66,11 @@ _ROUTER_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_k
                    "router_scalar.hip"]
 _LOSS_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",
                  "router_loss.hip"]
+_GATE_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",
+                 "router_topk_wave.h", "router_gate.hip"]
 SYMBOL_SOURCES = {"fwd_kernel": _ROUTER_SOURCES, "bwd_kernel": _ROUTER_SOURCES,
                   "loss_kernel": _LOSS_SOURCES, "count_kernel": _LOSS_SOURCES,
-                  "loss_bwd_kernel": _LOSS_SOURCES}
+                  "loss_bwd_kernel": _LOSS_SOURCES, "shared_gate_kernel": _GATE_SOURCES}
 
 
 def kernel_source_hash(symbol="fwd_kernel"):
@@ -80,10 +82,10 @@ def kernel_source_hash(symbol="fwd_kernel"):
     return h.hexdigest()[:16]
 
 
-def read_traffic(symbol):
+def read_traffic(symbol, workload="c4_2304x36"):
     """Measured HBM bytes per launch of kernel `symbol` from the committed
     profiler summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{symbol}_c4_2304x36.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{symbol}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -270,7 +272,7 @@ def shared_gate_bytes(M, E=512, H=4096, K=10, S=1, esz=2):
     return M * E * esz + M * H * esz + S * H * esz + M * (K + S) * 8
 
 
-def run_shared_gate(torch, router, synth, steps):
+def run_shared_gate(torch, router, synth, steps, only_m=None):
     """Routed top-k with the shared-expert gate at the aiter page's shape
     (E=512 experts, hidden 4096, top-10, one shared expert, bf16) over its
     token sweep; calls replayed from a HIP graph; from M=1024 on the inputs
@@ -278,7 +280,7 @@ def run_shared_gate(torch, router, synth, steps):
     dev = torch.device("cuda:0")
     E, H, K, S = 512, 4096, 10, 1
     out = {}
-    for M in (1, 4, 16, 64, 256, 1024, 4096, 16384):
+    for M in ((only_m,) if only_m else (1, 4, 16, 64, 256, 1024, 4096, 16384)):
         def dev_bf16(seed, shape, std):
             bits = synth.storage(synth.normal(seed, shape, std), synth.BF16)[0]
             return torch.from_numpy(bits.view("int16")).to(dev).view(torch.bfloat16)
@@ -297,9 +299,31 @@ def run_shared_gate(torch, router, synth, steps):
         out[f"M{M}"] = {"us_graph": round(us, 2), "GBps": round(nb / us / 1e3, 1),
                         "frac_of_peak": round(nb / us / 1e3 / PEAK_GBPS, 4),
                         "algo_bytes": nb, "cold": n > 1,
-                        "page_aiter_fused_us_context": PAGE_AITER_FUSED_US[M]}
+                        "page_aiter_fused_us_context": PAGE_AITER_FUSED_US.get(M)}
         del sets, x0, h0
     return out
+
+
+def copy_calibration(torch, dev, mib):
+    """A plain device copy of `mib` MiB (the profiler's scale reference for
+    byte counters), timed; None when mib is 0."""
+    if not mib:
+        return None
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        b.copy_(a)
+    c0.record()
+    for _ in range(10):
+        b.copy_(a)
+    c1.record()
+    torch.cuda.synchronize()
+    us = c0.elapsed_time(c1) * 100
+    return {"bytes_read": n, "bytes_written": n, "us_avg": round(us, 2),
+            "GBps": round(2 * n / us / 1e3, 1)}
 
 
 def run_decode_route(torch, router, synth, steps):
@@ -352,6 +376,8 @@ def main():
                     help="time only the decode routing (for profiler runs)")
     ap.add_argument("--only-shared-gate", action="store_true",
                     help="time only the shared-gate sweep (for profiler runs)")
+    ap.add_argument("--shared-gate-tokens", type=int, default=0,
+                    help="with --only-shared-gate: one token count instead of the sweep")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the T=8192 E/K sweep object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -374,8 +400,13 @@ def main():
         return
     if args.only_shared_gate:
         torch.cuda.set_device(0)
-        print(json.dumps({"shared_gate": run_shared_gate(torch, router, synth, args.steps)}),
-              flush=True)
+        res = {"shared_gate": run_shared_gate(torch, router, synth, args.steps,
+                                              args.shared_gate_tokens or None),
+               "kernel_source_hash": {"gate": kernel_source_hash("shared_gate_kernel")}}
+        copy = copy_calibration(torch, torch.device("cuda:0"), args.copy_calibration_mib)
+        if copy:
+            res["copy_calibration"] = copy
+        print(json.dumps(res), flush=True)
         return
 
     wl = synth.WORKLOADS[args.workload]
@@ -530,23 +561,7 @@ def main():
             "frac": round(nb / us / 1e3 / PEAK_GBPS, 4),
             "algo_bytes_per_launch": int(nb), "traffic": traffic}
 
-    copy = None
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
-        a.fill_(1)
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for _ in range(3):
-            b.copy_(a)
-        c0.record()
-        for _ in range(10):
-            b.copy_(a)
-        c1.record()
-        torch.cuda.synchronize()
-        us = c0.elapsed_time(c1) * 100
-        copy = {"bytes_read": n, "bytes_written": n, "us_avg": round(us, 2),
-                "GBps": round(2 * n / us / 1e3, 1)}
+    copy = copy_calibration(torch, dev, args.copy_calibration_mib)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -570,7 +585,8 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
         "device": torch.cuda.get_device_name(0),
         "kernel_source_hash": {"router": kernel_source_hash("fwd_kernel"),
-                               "loss": kernel_source_hash("loss_kernel")},
+                               "loss": kernel_source_hash("loss_kernel"),
+                               "gate": kernel_source_hash("shared_gate_kernel")},
     }
     if not args.only:
         loss = {}
@@ -606,6 +622,9 @@ def main():
             "decode-shape routing with expert maps (one workgroup): microseconds per call, "
             "T rows x E=512 experts x K, softmax renormalised, fp32")
         out["shared_gate"] = run_shared_gate(torch, router, synth, max(10, args.steps // 4))
+        m16 = out["shared_gate"]["M16384"]
+        m16["traffic"] = (read_traffic("shared_gate_kernel", "e512_h4096_m16384")
+                          if not args.warm else None)
         out["shared_gate_note"] = (
             "routed softmax top-k with the shared-expert sigmoid gate: M tokens x E=512 x "
             "hidden 4096, top-10, one shared expert, bf16, renormalised; graph-replayed; "

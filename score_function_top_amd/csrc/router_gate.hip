@@ -9,7 +9,8 @@
 // stated in include/router.h.
 //
 // One wave per token (grid-stride over tokens).  The routed half is the
-// ordered top-K of router_topk_wave.h.  The gate half is a GEMV with S <= 16
+// ordered top-K of router_topk_wave.h; a hidden row of up to 8 pieces per
+// lane is requested before it.  The gate half is a GEMV with S <= 16
 // outputs per token, bound by the hidden-state read (H elements per token,
 // S flops each): it runs on the VALU, not on matrix cores.  Lane l owns
 // the 16-byte pieces h = c*64*VH + VH*l (VH elements per piece); each piece
@@ -75,7 +76,27 @@ __device__ __forceinline__ void load16(rsrc_t r, int h, int H, uint32_t (&v)[4])
     }
 }
 
-template <int NCH, typename TIn, bool VEC_G, bool VEC_H>
+// Row m of the outputs: K routed slots (lane k < K), then S gates (lane
+// K + s).
+__device__ __forceinline__ void store_row(const GateParams &p, int64_t m, int lane, int id,
+                                          float wt, float gate)
+{
+    const uint32_t nb = (uint32_t)(p.K + p.S) * 4u;
+    const rsrc_t rw = make_rsrc(p.weights + m * p.ld, nb);
+    const rsrc_t ri = make_rsrc(p.ids + m * p.ld, nb);
+    const bool routed = lane < p.K;
+    const bool shared = lane >= p.K && lane < p.K + p.S;
+    const uint32_t o = routed || shared ? (uint32_t)lane * 4u : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b32(as_u(routed ? wt : gate), rw, (int)o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(routed ? id : p.base + (lane - p.K)), ri,
+                                          (int)o, 0, 0);
+}
+
+// Hidden-row pieces (16 bytes per lane) requested before the routed half
+// when the whole row fits: 4096 bf16 or 2048 fp32 elements.
+constexpr int kGatePrefetch = 8;
+
+template <int NCH, typename TIn, bool VEC_G, bool VEC_H, bool PRE>
 __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
 {
     __shared__ uint64_t cand[kWaves][kSortedSlots];
@@ -89,6 +110,16 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
     for (int64_t m = (int64_t)blockIdx.x * kWaves + wave; m < p.M; m += nwaves) {
+        const rsrc_t rh = make_rsrc((const char *)p.hs + m * H * sz, (uint32_t)H * sz);
+        [[maybe_unused]] uint32_t hpre[kGatePrefetch][4];
+        if constexpr (PRE) {
+            // the whole hidden row is requested before the routed half, so
+            // its latency hides behind that work
+#pragma unroll
+            for (int c = 0; c < kGatePrefetch; c++)
+                load16<TIn, VEC_H, kStream>(rh, c * 64 * VH + VH * lane, H, hpre[c]);
+        }
+
         // routed half
         const rsrc_t rx = make_rsrc((const char *)p.x + m * E * sz, (uint32_t)E * sz);
         int id;
@@ -96,7 +127,23 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
         wave_topk_row<NCH, TIn, VEC_G>(rx, E, K, SCORE_SOFTMAX, p.renorm, cand[wave], id, wt);
 
         // gate half: S dot products over the hidden row
-        const rsrc_t rh = make_rsrc((const char *)p.hs + m * H * sz, (uint32_t)H * sz);
+        if constexpr (PRE) {
+            float gate = 0.0f;
+            for (int s = 0; s < S; s++) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int c = 0; c < kGatePrefetch; c++) {
+                    const int h = c * 64 * VH + VH * lane;
+                    uint32_t gv[4];
+                    load16<TIn, VEC_H, 0>(rgw, s * H + h, s * H + H, gv);
+                    acc = dot16<TIn>(hpre[c], gv, acc);
+                }
+                const float logit = group_sum<64>(acc);
+                gate = lane == K + s ? p.scale * sigmoid_fast(logit) : gate;
+            }
+            store_row(p, m, lane, id, wt, gate);
+            continue;
+        }
         float acc[kGateMaxShared];
 #pragma unroll
         for (int s = 0; s < kGateMaxShared; s++)
@@ -124,32 +171,32 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
             }
         }
 
-        // row m of the outputs: K routed slots, then S gates
-        const uint32_t nb = (uint32_t)(K + S) * 4u;
-        const rsrc_t rw = make_rsrc(p.weights + m * p.ld, nb);
-        const rsrc_t ri = make_rsrc(p.ids + m * p.ld, nb);
-        const bool routed = lane < K;
-        const bool shared = lane >= K && lane < K + S;
-        const uint32_t o = routed || shared ? (uint32_t)lane * 4u : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b32(as_u(routed ? wt : gate), rw, (int)o, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(
-            (uint32_t)(routed ? id : p.base + (lane - K)), ri, (int)o, 0, 0);
+        store_row(p, m, lane, id, wt, gate);
     }
+}
+
+template <int NCH, typename TIn, bool PRE>
+hipError_t gate_p(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hipStream_t st)
+{
+    const dim3 g(grid), b(kBlock);
+    if (vec_g && vec_h)
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, true, PRE>), g, b, 0, st, p);
+    else if (vec_g)
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, false, PRE>), g, b, 0, st, p);
+    else if (vec_h)
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, true, PRE>), g, b, 0, st, p);
+    else
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, false, PRE>), g, b, 0, st, p);
+    return hipGetLastError();
 }
 
 template <int NCH, typename TIn>
 hipError_t gate_t(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hipStream_t st)
 {
-    const dim3 g(grid), b(kBlock);
-    if (vec_g && vec_h)
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, true>), g, b, 0, st, p);
-    else if (vec_g)
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, false>), g, b, 0, st, p);
-    else if (vec_h)
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, true>), g, b, 0, st, p);
-    else
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, false>), g, b, 0, st, p);
-    return hipGetLastError();
+    const int vh = 16 / (int)sizeof(TIn);
+    const bool pre = vec_h && p.H <= kGatePrefetch * 64 * vh;
+    return pre ? gate_p<NCH, TIn, true>(p, vec_g, vec_h, grid, st)
+               : gate_p<NCH, TIn, false>(p, vec_g, vec_h, grid, st);
 }
 
 template <int NCH>

@@ -314,6 +314,21 @@ const char *router_status_str(router_status s);
 int router_get_topk_path_threshold(void);
 router_status router_set_topk_path_threshold(int threshold);
 
+/*
+ * Group stage of the group-limited forward.  Passage: the fused-router
+ * page, "Forward kernels" (group-limited routing inside the fused kernel).
+ * ROUTER_GROUP_STAGE_AUTO (default) scores the groups in registers when
+ * each group of E/num_groups experts is 4*L experts with L a power of two
+ * that fits the kernel's lane layout, and through an LDS scratch copy of
+ * the row otherwise; ROUTER_GROUP_STAGE_LDS always takes the LDS copy.
+ * Both give the same scores, maps and outputs.  A process-wide setting;
+ * other values return ROUTER_ERR_INVALID_ARG.
+ */
+#define ROUTER_GROUP_STAGE_AUTO 0
+#define ROUTER_GROUP_STAGE_LDS 1
+int router_get_group_stage(void);
+router_status router_set_group_stage(int stage);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,8 @@ int threshold()
     return g_threshold.load();
 }
 
+std::atomic<int> g_group_stage{ROUTER_GROUP_STAGE_AUTO};
+
 // ------------------------------------------------------------ devices
 
 struct DevInfo {
@@ -144,16 +146,35 @@ bool fill_nch(Cfg &c, int E)
 
 int widen(int lpt, int need) { return need <= lpt ? lpt : (need <= 32 ? 32 : 64); }
 
-hipError_t launch_fwd(const Cfg &c, int dtype, int score, bool grouped, const FwdParams &p,
+// log2 of the lanes per group when the register group stage can take G
+// groups of E/G experts in the layout c with q = K/Kg summed per group:
+// E/G = 4*L with L a power of two no larger than the lane width, at most
+// kGroupRegSlots group slots, a vector kernel of at most kGroupRegMaxNch
+// chunks, q <= 4.  -1 otherwise.
+int group_reg_log(const Cfg &c, int E, int G, int q)
+{
+    const int P = E / G;
+    if (!c.vec || c.nch > kGroupRegMaxNch || q > 4 || P % 4 != 0)
+        return -1;
+    const int L = P / 4;
+    if ((L & (L - 1)) != 0)
+        return -1;
+    int lg = 0;
+    while ((1 << lg) < L)
+        lg++;
+    return group_reg_ok(c.lpt, c.nch, lg) ? lg : -1;
+}
+
+hipError_t launch_fwd(const Cfg &c, int dtype, int score, int gm, const FwdParams &p,
                       const Launch &l)
 {
     hipError_t err = hipErrorInvalidValue;
-    if (fwd_lpt16(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
-        fwd_lpt32(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
-        fwd_lpt64a(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
-        fwd_lpt64b(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
-        fwd_lpt64c(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err) ||
-        fwd_scalar(c.lpt, c.nch, c.vec, dtype, score, grouped, p, l, &err))
+    if (fwd_lpt16(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
+        fwd_lpt32(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
+        fwd_lpt64a(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
+        fwd_lpt64b(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
+        fwd_lpt64c(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
+        fwd_scalar(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err))
         return err;
     return hipErrorInvalidValue;
 }
@@ -220,12 +241,16 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     if (sel == SEL_PRUNE && K > c.lpt)
         sel = SEL_BITS;
 
+    const bool reg = g_group_stage.load() == ROUTER_GROUP_STAGE_AUTO && G > 0 &&
+                     group_reg_log(c, E, G, K / Kg) >= 0;
+    const int gm = G == 0 ? GROUP_NONE : (reg ? GROUP_REG : GROUP_LDS);
+
     DevInfo dev;
     if (dev_info(&dev) != hipSuccess)
         return ROUTER_ERR_HIP;
     const int tpb = kWaves * (64 / c.lpt);
     size_t smem = (size_t)tpb * cand_slots(c.lpt) * sizeof(uint64_t);
-    if (G > 0)
+    if (gm == GROUP_LDS)
         smem += (size_t)tpb * group_scratch_floats(E, G, c.lpt) * sizeof(float);
     if (smem > dev.lds_per_block)
         return ROUTER_ERR_UNSUPPORTED;
@@ -246,9 +271,10 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     p.Kg = G > 0 ? Kg : 0;
     p.q = G > 0 ? K / Kg : 0;
     p.P = G > 0 ? E / G : 0;
+    p.glog = gm == GROUP_REG ? group_reg_log(c, E, G, K / Kg) : 0;
     p.scale = scale;
     const Launch l{grid_for(T, c.lpt), smem, (hipStream_t)stream};
-    return launch_fwd(c, dtype, score_fn, G > 0, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+    return launch_fwd(c, dtype, score_fn, gm, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
 router_status bwd_common(const void *g, const float *s, const uint8_t *m, int dtype, int64_t T,
@@ -552,6 +578,16 @@ router_status router_set_topk_path_threshold(int t)
         return ROUTER_ERR_INVALID_ARG;
     threshold();  // the environment is read first, then overridden
     g_threshold.store(t);
+    return ROUTER_OK;
+}
+
+int router_get_group_stage(void) { return g_group_stage.load(); }
+
+router_status router_set_group_stage(int stage)
+{
+    if (stage != ROUTER_GROUP_STAGE_AUTO && stage != ROUTER_GROUP_STAGE_LDS)
+        return ROUTER_ERR_INVALID_ARG;
+    g_group_stage.store(stage);
     return ROUTER_OK;
 }
 

@@ -32,6 +32,8 @@
 // the buffer's range, which the hardware drops.
 #pragma once
 
+#include <type_traits>
+
 #include "router_device.h"
 #include "router_io.h"
 #include "router_params.h"
@@ -414,13 +416,192 @@ __device__ __forceinline__ void group_limit(float (&key)[NCH][4], const FwdParam
     __builtin_amdgcn_wave_barrier();
 }
 
+// Group-limited routing in registers, for groups that tile the chunk
+// layout: P = 4*L with L a power of two no larger than LPT, so group g
+// of a row is lanes [s*L, (s+1)*L) of chunk c with g = c*(LPT/L) + s, and
+// each lane's four elements of a chunk share one group.  The same result
+// as group_limit (same group scores, bit for bit, and the same kept
+// groups), without LDS: each lane sorts its four values, the lists merge
+// across the L lanes of the group (the merge steps of group_allreduce_u
+// whose lane distance is below L), and every lane ranks its groups against
+// all others, read with one cross-lane permute per group slot.
+//
+// Merge of two descending lists a, b of length Q into the Q largest of
+// both, descending: max(a_i, b_{Q-1-i}) holds exactly those values in a
+// V-shaped order, which one bitonic pass sorts.
+template <int Q>
+__device__ __forceinline__ void topq_merge(float (&a)[Q], const float (&b)[Q])
+{
+    float c[Q];
+#pragma unroll
+    for (int i = 0; i < Q; i++)
+        c[i] = fmaxf(a[i], b[Q - 1 - i]);
+    if constexpr (Q == 2) {
+        a[0] = fmaxf(c[0], c[1]);
+        a[1] = fminf(c[0], c[1]);
+    } else {
+        static_assert(Q == 4, "lists of 2 or 4");
+        const float h0 = fmaxf(c[0], c[2]), l0 = fminf(c[0], c[2]);
+        const float h1 = fmaxf(c[1], c[3]), l1 = fminf(c[1], c[3]);
+        a[0] = fmaxf(h0, h1);
+        a[1] = fminf(h0, h1);
+        a[2] = fmaxf(l0, l1);
+        a[3] = fminf(l0, l1);
+    }
+}
+
+// The Q largest of four values, descending.
+template <int Q>
+__device__ __forceinline__ void topq_of4(const float (&x)[4], float (&t)[Q])
+{
+    const float a = fmaxf(x[0], x[1]), b = fminf(x[0], x[1]);
+    const float c = fmaxf(x[2], x[3]), d = fminf(x[2], x[3]);
+    if constexpr (Q == 2) {
+        t[0] = fmaxf(a, c);
+        t[1] = fmaxf(fminf(a, c), fmaxf(b, d));
+    } else {
+        static_assert(Q == 4, "lists of 2 or 4");
+        t[0] = fmaxf(a, c);
+        t[3] = fminf(b, d);
+        const float m1 = fminf(a, c), m2 = fmaxf(b, d);
+        t[1] = fmaxf(m1, m2);
+        t[2] = fminf(m1, m2);
+    }
+}
+
+// One merge step with the list of the lane at distance D (lane ^ D for
+// D = 1, 2; the mirror image inside blocks of 2D lanes from D = 4 on, which
+// pairs blocks of D lanes that already agree).
+template <int D, int Q>
+__device__ __forceinline__ void topq_step(float (&t)[Q])
+{
+    float o[Q];
+#pragma unroll
+    for (int i = 0; i < Q; i++) {
+        const uint32_t v = as_u(t[i]);
+        uint32_t w;
+        if constexpr (D == 1)
+            w = dpp_mov<kQpXor1>(v);
+        else if constexpr (D == 2)
+            w = dpp_mov<kQpXor2>(v);
+        else if constexpr (D == 4)
+            w = dpp_mov<kRowHalfMirror>(v);
+        else if constexpr (D == 8)
+            w = dpp_mov<kRowMirror>(v);
+        else
+            w = shfl_xor<D>(v);
+        o[i] = as_f(w);
+    }
+    topq_merge<Q>(t, o);
+}
+
+// Group stage for 2^LG lanes per group and lists of Q values (q <= Q).
+template <int LPT, int NCH, int LG, int Q>
+__device__ __forceinline__ void group_limit_reg_t(float (&key)[NCH][4],
+                                                  const float (&s)[NCH][4], bool has_bias,
+                                                  const FwdParams &p, int lane)
+{
+    constexpr int L = 1 << LG;
+    constexpr int NS = LPT / L;  // groups per chunk
+    float h[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            x[u] = has_bias ? key[c][u] : s[c][u];  // s + b (the keys hold it with a bias)
+        float t[Q];
+        topq_of4<Q>(x, t);
+        if constexpr (L > 1)
+            topq_step<1, Q>(t);
+        if constexpr (L > 2)
+            topq_step<2, Q>(t);
+        if constexpr (L > 4)
+            topq_step<4, Q>(t);
+        if constexpr (L > 8)
+            topq_step<8, Q>(t);
+        if constexpr (L > 16)
+            topq_step<16, Q>(t);
+        if constexpr (L > 32)
+            topq_step<32, Q>(t);
+        float a = t[0];
+#pragma unroll
+        for (int i = 1; i < Q; i++)
+            a = p.q > i ? a + t[i] : a;
+        h[c] = a;
+    }
+
+    // every lane reads all S = NCH*NS group slots; lane i < S ranks slot i
+    // among the G real ones (ties: lower group; slots past G are padding
+    // past E), and one ballot hands the kept groups to every lane
+    constexpr int S = NCH * NS;
+    static_assert(S <= LPT, "one lane per group slot");
+    const int base = lane_id() & ~(LPT - 1);
+    float o[S];
+#pragma unroll
+    for (int c2 = 0; c2 < NCH; c2++)
+#pragma unroll
+        for (int s2 = 0; s2 < NS; s2++)
+            o[c2 * NS + s2] = as_f((uint32_t)__builtin_amdgcn_ds_bpermute(
+                (base + s2 * L) << 2, (int)as_u(h[c2])));
+    float mine = o[0];
+#pragma unroll
+    for (int g = 1; g < S; g++)
+        mine = lane == g ? o[g] : mine;
+    uint32_t rank = 0;
+#pragma unroll
+    for (int g2 = 0; g2 < S; g2++) {
+        // bitwise, so no branch per comparison
+        const uint32_t beats = (uint32_t)(o[g2] > mine) |
+                               ((uint32_t)(o[g2] == mine) & (uint32_t)(g2 < lane));
+        rank += g2 < p.G ? beats : 0u;
+    }
+    const bool kept_slot = (lane < p.G) & (rank < (uint32_t)p.Kg);
+    const uint64_t kept = __builtin_amdgcn_ballot_w64(kept_slot) >> base;
+    const int seg = lane >> LG;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const bool in = (kept >> (c * NS + seg)) & 1u;
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            key[c][u] = in ? key[c][u] : -INFINITY;
+    }
+}
+
+// Dispatch on the lanes per group (p.glog) and the list length; the host
+// takes this stage only for the combinations built here (group_reg_ok).
+template <int LPT, int NCH>
+__device__ __forceinline__ void group_limit_reg(float (&key)[NCH][4], const float (&s)[NCH][4],
+                                                bool has_bias, const FwdParams &p, int lane)
+{
+    auto run = [&](auto lg) {
+        constexpr int LG = decltype(lg)::value;
+        if constexpr (group_reg_ok(LPT, NCH, LG)) {
+            if (p.q <= 2)
+                group_limit_reg_t<LPT, NCH, LG, 2>(key, s, has_bias, p, lane);
+            else
+                group_limit_reg_t<LPT, NCH, LG, 4>(key, s, has_bias, p, lane);
+        }
+    };
+    switch (p.glog) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 5: run(std::integral_constant<int, 5>{}); break;
+    default: run(std::integral_constant<int, 6>{}); break;
+    }
+}
+
 // ------------------------------------------------------------ forward
 
 // SEL_ARGMAX kernels run the argmax rounds; SEL_PRUNE kernels run the
-// pruned sort, or the bit search when p.sel == SEL_BITS.  GROUPED kernels
-// add group-limited routing (p.G > 0).
-template <int LPT, int NCH, typename TIn, int SCORE, int SEL, bool GROUPED, bool VEC>
-__global__ void __launch_bounds__(kBlock, GROUPED && VEC && NCH <= 4 ? 3 : 1)
+// pruned sort, or the bit search when p.sel == SEL_BITS.  GM selects
+// group-limited routing (p.G > 0): GROUP_NONE, GROUP_LDS (group_limit, any
+// P) or GROUP_REG (group_limit_reg, groups that tile the chunks).
+template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC>
+__global__ void __launch_bounds__(kBlock, GM == GROUP_LDS && VEC && NCH <= 4 ? 3 : (GM == GROUP_REG ? 4 : 1))
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave
@@ -492,12 +673,12 @@ fwd_kernel(FwdParams p)
         // ---- expert bias (selection only) and group values s + b
         [[maybe_unused]] float *gscr = nullptr;
         [[maybe_unused]] float invP = 0.0f;
-        if constexpr (GROUPED) {
+        if constexpr (GM == GROUP_LDS) {
             gscr = reinterpret_cast<float *>(smem + TPB * cand_slots(LPT)) +
                    gslot * group_scratch_floats(E, p.G, LPT);
             invP = 1.0f / (float)p.P;
         }
-        if (has_bias || GROUPED) {
+        if (has_bias || GM == GROUP_LDS) {
             const rsrc_t rb = make_rsrc(p.bias, has_bias ? (uint32_t)E * 4u : 0u);
 #pragma unroll
             for (int c = 0; c < NCH; c++) {
@@ -508,15 +689,17 @@ fwd_kernel(FwdParams p)
                 for (int u = 0; u < 4; u++) {
                     const float r = s[c][u] + b[u];
                     const bool real = key[c][u] != -INFINITY;
-                    if constexpr (GROUPED)
+                    if constexpr (GM == GROUP_LDS)
                         group_value_store(gscr, jrel<LPT>(c, u) + j_lane, real, r, p, invP, lane);
                     if (has_bias)
                         key[c][u] = real ? r : -INFINITY;
                 }
             }
         }
-        if constexpr (GROUPED)
+        if constexpr (GM == GROUP_LDS)
             group_limit<LPT, NCH>(key, p, lane, j_lane, tok, invP, gscr);
+        if constexpr (GM == GROUP_REG)
+            group_limit_reg<LPT, NCH>(key, s, has_bias, p, lane);
 
         // ---- top-K; the selection lives in the map words (one byte per
         // element, chunk-packed), which the store needs anyway

@@ -16,26 +16,32 @@
 
 namespace rker {
 
-template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
-hipError_t fwd_one(const FwdParams &p, bool grouped, const Launch &l)
+template <int LPT, int NCH, typename TIn, int SCORE, int SEL, bool VEC>
+hipError_t fwd_sel(const FwdParams &p, int gm, const Launch &l)
 {
     dim3 g(l.grid), b(kBlock);
-    if (p.sel == SEL_ARGMAX) {
-        if (grouped)
-            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_ARGMAX, true, VEC>), g, b,
+    if (gm == GROUP_LDS) {
+        hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_LDS, VEC>), g, b,
+                           l.smem, l.stream, p);
+    } else if (gm == GROUP_REG) {
+        // built for vector kernels of up to kGroupRegMaxNch chunks only
+        if constexpr (VEC && NCH <= kGroupRegMaxNch)
+            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_REG, VEC>), g, b,
                                l.smem, l.stream, p);
         else
-            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_ARGMAX, false, VEC>), g, b,
-                               l.smem, l.stream, p);
+            return hipErrorInvalidValue;
     } else {
-        if (grouped)
-            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_PRUNE, true, VEC>), g, b,
-                               l.smem, l.stream, p);
-        else
-            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL_PRUNE, false, VEC>), g, b,
-                               l.smem, l.stream, p);
+        hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_NONE, VEC>), g, b,
+                           l.smem, l.stream, p);
     }
     return hipGetLastError();
+}
+
+template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
+hipError_t fwd_one(const FwdParams &p, int gm, const Launch &l)
+{
+    return p.sel == SEL_ARGMAX ? fwd_sel<LPT, NCH, TIn, SCORE, SEL_ARGMAX, VEC>(p, gm, l)
+                               : fwd_sel<LPT, NCH, TIn, SCORE, SEL_PRUNE, VEC>(p, gm, l);
 }
 
 template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
@@ -48,17 +54,17 @@ hipError_t bwd_one(const BwdParams &p, const Launch &l)
 
 // Launches the forward for the first listed N equal to nch.
 template <int LPT, bool VEC, int... N>
-bool fwd_pick(int nch, int dtype, int score, bool grouped, const FwdParams &p,
+bool fwd_pick(int nch, int dtype, int score, int gm, const FwdParams &p,
               const Launch &l, hipError_t *err)
 {
     auto one = [&](auto nc) {
         constexpr int C = decltype(nc)::value;
         if (dtype == 0)
-            *err = score == 0 ? fwd_one<LPT, C, float, 0, VEC>(p, grouped, l)
-                              : fwd_one<LPT, C, float, 1, VEC>(p, grouped, l);
+            *err = score == 0 ? fwd_one<LPT, C, float, 0, VEC>(p, gm, l)
+                              : fwd_one<LPT, C, float, 1, VEC>(p, gm, l);
         else
-            *err = score == 0 ? fwd_one<LPT, C, uint16_t, 0, VEC>(p, grouped, l)
-                              : fwd_one<LPT, C, uint16_t, 1, VEC>(p, grouped, l);
+            *err = score == 0 ? fwd_one<LPT, C, uint16_t, 0, VEC>(p, gm, l)
+                              : fwd_one<LPT, C, uint16_t, 1, VEC>(p, gm, l);
         return true;
     };
     return ((nch == N && one(std::integral_constant<int, N>{})) || ...);
@@ -87,12 +93,12 @@ bool bwd_pick(int nch, int dtype, int score, const BwdParams &p, const Launch &l
 // listed chunk counts.
 #define ROUTER_DEFINE_PART(NAME, LPT_, VEC_, ...)                                   \
     namespace rker {                                                                \
-    bool fwd_##NAME(int lpt, int nch, bool vec, int dtype, int score, bool grouped, \
+    bool fwd_##NAME(int lpt, int nch, bool vec, int dtype, int score, int gm,       \
                     const FwdParams &p, const Launch &l, hipError_t *err)           \
     {                                                                               \
         if (lpt != LPT_ || vec != VEC_)                                             \
             return false;                                                           \
-        return fwd_pick<LPT_, VEC_, __VA_ARGS__>(nch, dtype, score, grouped, p, l,  \
+        return fwd_pick<LPT_, VEC_, __VA_ARGS__>(nch, dtype, score, gm, p, l,       \
                                                  err);                              \
     }                                                                               \
     bool bwd_##NAME(int lpt, int nch, bool vec, int dtype, int score,               \

@@ -14,6 +14,22 @@ constexpr int kWaves = kBlock / 64;
 
 enum { SEL_ARGMAX = 0, SEL_PRUNE = 1, SEL_BITS = 2 };
 enum { SCORE_SOFTMAX = 0, SCORE_SIGMOID = 1 };
+// Group stage of the forward: none, LDS scratch (any group size), or
+// registers (groups of 4*L experts, L a power of two up to the lane width,
+// so each lane's four elements of a chunk share one group).
+enum { GROUP_NONE = 0, GROUP_LDS = 1, GROUP_REG = 2 };
+
+// Register group stage: at most this many group slots (chunks times groups
+// per chunk) per token, and chunk counts it is built for.
+constexpr int kGroupRegSlots = 16;
+constexpr int kGroupRegMaxNch = 4;
+// Built (lanes per token LPT, chunks NCH, log2 of lanes per group LG):
+// L = 2^LG <= LPT and NCH * LPT / L <= kGroupRegSlots group slots.
+constexpr bool group_reg_ok(int lpt, int nch, int lg)
+{
+    return nch <= kGroupRegMaxNch && lg >= 0 && (1 << lg) <= lpt &&
+           nch * (lpt >> lg) <= kGroupRegSlots;
+}
 
 struct FwdParams {
     const void *x;        // logits [T,E], TIn
@@ -32,6 +48,7 @@ struct FwdParams {
     int Kg;               // groups kept
     int q;                // K / Kg
     int P;                // E / G
+    int glog;             // GROUP_REG: log2 of the lanes per group (P / 4)
     float scale;          // scaling factor (topk)
 };
 
@@ -222,7 +239,7 @@ constexpr int kNchScalar[] = {1, 2, 4, 8, 16};
 // Each translation unit of kernels defines one pair; they return false when
 // the (LPT, NCH, vec) configuration is not built there.
 #define ROUTER_DECLARE_PART(NAME)                                                   \
-    bool fwd_##NAME(int lpt, int nch, bool vec, int dtype, int score, bool grouped, \
+    bool fwd_##NAME(int lpt, int nch, bool vec, int dtype, int score, int gm,       \
                     const FwdParams &p, const Launch &l, hipError_t *err);          \
     bool bwd_##NAME(int lpt, int nch, bool vec, int dtype, int score,               \
                     const BwdParams &p, const Launch &l, hipError_t *err);

@@ -75,6 +75,10 @@ def load():
     lib.router_set_topk_path_threshold.argtypes = [ci]
     lib.router_get_topk_path_threshold.argtypes = []
     lib.router_get_topk_path_threshold.restype = ci
+    lib.router_set_group_stage.argtypes = [ci]
+    lib.router_set_group_stage.restype = ci
+    lib.router_get_group_stage.argtypes = []
+    lib.router_get_group_stage.restype = ci
     lib.router_status_str.argtypes = [ci]
     lib.router_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -96,6 +100,18 @@ def set_topk_path_threshold(threshold):
 
 def get_topk_path_threshold():
     return load().router_get_topk_path_threshold()
+
+
+GROUP_STAGE_AUTO = 0
+GROUP_STAGE_LDS = 1
+
+
+def set_group_stage(stage):
+    check(load().router_set_group_stage(int(stage)))
+
+
+def get_group_stage():
+    return load().router_get_group_stage()
 
 
 def _ptr(t):

@@ -125,6 +125,20 @@ def test_threshold_setter():
         router.set_topk_path_threshold(old)
 
 
+def test_group_stage_setter():
+    assert router.get_group_stage() == router.GROUP_STAGE_AUTO
+    try:
+        router.set_group_stage(router.GROUP_STAGE_LDS)
+        assert router.get_group_stage() == router.GROUP_STAGE_LDS
+        for bad in (-1, 2):
+            with pytest.raises(router.RouterError) as e:
+                router.set_group_stage(bad)
+            assert e.value.status == INV
+        assert router.get_group_stage() == router.GROUP_STAGE_LDS
+    finally:
+        router.set_group_stage(router.GROUP_STAGE_AUTO)
+
+
 @pytest.mark.parametrize("env,expect", [(None, 8), ("3", 3), ("0", 0), ("abc", 8),
                                         ("-4", 8), ("5000", 8), ("12x", 8)])
 def test_threshold_environment(env, expect):

@@ -198,6 +198,74 @@ def test_grouped_softmax():
     run_fwd(edge_wl(300, 256, 8, synth.SOFTMAX, True, G=8, Kg=4, seed=13))
 
 
+# Shapes the register group stage takes (4*L experts per group, L a power of
+# two up to the lanes per token, at most 16 group slots, q <= 4).
+GROUP_STAGE_CASES = [
+    (500, 256, 8, 8, 4, synth.BF16, synth.SIGMOID, 0.05),   # 8 lanes per group, q = 2
+    (257, 256, 16, 8, 4, synth.BF16, synth.SIGMOID, 0.0),   # q = 4
+    (200, 64, 6, 4, 2, synth.F32, synth.SIGMOID, 0.05),     # 4 lanes, one chunk
+    (90, 96, 12, 12, 4, synth.F32, synth.SIGMOID, 0.0),     # 2 lanes, q = 3, 16 slots
+    (70, 160, 9, 10, 3, synth.F32, synth.SOFTMAX, 0.0),     # slots past E
+    (129, 512, 22, 16, 11, synth.F32, synth.SIGMOID, 0.05), # 32-lane tokens
+    (100, 512, 16, 4, 4, synth.F32, synth.SIGMOID, 0.0),    # a group fills a chunk
+    (64, 1024, 8, 8, 4, synth.F32, synth.SIGMOID, 0.05),    # 64-lane tokens
+    (65, 768, 12, 6, 3, synth.BF16, synth.SOFTMAX, 0.0),    # three chunks
+]
+
+
+def _group_stage_outputs(wl, x_st, stage):
+    router.set_group_stage(stage)
+    try:
+        bias = wl.bias()
+        bt = None if bias is None else torch.from_numpy(bias).to(DEV)
+        out = router.router_topk_fwd(to_dev(x_st, wl.dtype), wl.K, SCORE_NAME[wl.score_fn],
+                                     wl.renorm, wl.num_groups, wl.group_topk,
+                                     wl.scaling_factor, bt)
+        torch.cuda.synchronize()
+    finally:
+        router.set_group_stage(router.GROUP_STAGE_AUTO)
+    return out
+
+
+@pytest.mark.parametrize("T,E,K,G,Kg,dtype,sf,b", GROUP_STAGE_CASES)
+def test_group_stage_parity(T, E, K, G, Kg, dtype, sf, b):
+    """The register and the LDS group stages agree bit for bit (same group
+    scores, so the same maps and outputs), on random logits and on integer
+    logits whose groups tie; the register stage matches the oracle on both,
+    exactly on the map where groups tie."""
+    wl = edge_wl(T, E, K, sf, True, bias=b, G=G, Kg=Kg, dtype=dtype, c=2.5, seed=29)
+    run_fwd(wl)
+
+    def cast(x):
+        return (x.astype(np.float32) if dtype == synth.F32 else
+                synth.f32_to_bf16_bits(x.astype(np.float32)))
+
+    rng = np.random.default_rng(T + E)
+    xi = rng.integers(-2, 3, (T, E)).astype(np.float64)
+    xi[1] = 1.0                       # every group ties
+    x_st, _ = wl.logits()
+    for name, xs in (("random", x_st), ("integer", cast(xi))):
+        say(f"[group stage] {wl.name} {name}")
+        reg = _group_stage_outputs(wl, xs, router.GROUP_STAGE_AUTO)
+        lds = _group_stage_outputs(wl, xs, router.GROUP_STAGE_LDS)
+        for u, v in zip(reg, lds):
+            assert torch.equal(u, v), f"{wl.name} {name}: group stages differ"
+
+    # Logits in {0, 1, 2} and no bias: groups tie exactly when their top-q
+    # multisets are equal (the lower group wins), and otherwise differ by far
+    # more than rounding, so the map is exact.
+    nob = dataclasses.replace(wl, bias_range=0.0, name=wl.name + "_ties")
+    xo = rng.integers(0, 3, (T, E)).astype(np.float64)
+    xo[1] = 1.0
+    xo_st = cast(xo)
+    x64 = xo if dtype == synth.F32 else synth.bf16_bits_to_f32(xo_st).astype(np.float64)
+    P, M, _, _ = oracle.topk_fwd(x64, K, sf, True, G, Kg, 2.5, threads=threads())
+    say(f"[group stage] {nob.name} against the oracle")
+    reg = _group_stage_outputs(nob, xo_st, router.GROUP_STAGE_AUTO)
+    assert (f64(reg[1]) == M).all(), f"{nob.name}: map differs from the oracle"
+    assert_close(f64(reg[0]), P, dtype, f"{nob.name} probs")
+
+
 def test_bf16_paths():
     for sf in (synth.SOFTMAX, synth.SIGMOID):
         for E, K in ((256, 4), (512, 22), (2304, 36), (100, 5)):

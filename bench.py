@@ -101,6 +101,128 @@ def read_traffic(symbol, workload="c4_2304x36"):
         return None
 
 
+def read_valu(symbol, workload="c4_2304x36"):
+    """VALU issue of kernel `symbol` from the committed counter summary
+    (SQ_ACTIVE_INST_VALU in 4-cycle units per launch, and VALU instructions
+    per wave), if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"valu_{symbol}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash(symbol):
+        return None
+    try:
+        return {"active_valu_quads_per_launch": float(vals["active_valu_quads_per_launch"]),
+                "valu_insts_per_wave": float(vals["valu_insts_per_wave"]),
+                "simds": int(vals["simds"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def valu_busy(valu, us, clock_khz):
+    """Share of the kernel's time the VALUs issue: SQ_ACTIVE_INST_VALU x 4
+    cycles over (SIMDs x duration x engine clock)."""
+    if not valu or not clock_khz:
+        return None
+    valu_us = valu["active_valu_quads_per_launch"] * 4 / valu["simds"] / (clock_khz * 1e-3)
+    return {"valu_us_per_launch": round(valu_us, 2), "busy": round(valu_us / us, 3),
+            "valu_insts_per_wave": valu["valu_insts_per_wave"]}
+
+
+def environment(torch, router):
+    """GPU, clocks, ROCm and the build the timed library came from."""
+    env = {"gpu": torch.cuda.get_device_name(0),
+           "arch": torch.cuda.get_device_properties(0).gcnArchName,
+           "torch_hip": torch.version.hip}
+    try:
+        env.update(router.device_query())
+    except router.RouterError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    info = os.path.join(ROOT, "score_function_top_amd", "librouter.build.json")
+    try:
+        with open(info) as f:
+            b = json.load(f)
+        env["hipcc"] = b.get("hipcc")
+        env["hipcc_flags"] = " ".join(b.get("flags", []))
+        env["built_from_git"] = b.get("git")
+    except (OSError, ValueError):
+        env["build_info"] = None
+    return env
+
+
+def oracle_gbps(synth, wl, thr, kinds, T=None):
+    """Oracle GB/s (median of 3 runs, same byte formula as the GPU) per
+    pass over the first T tokens of `wl`."""
+    import numpy as np
+    import oracle
+    T = T or wl.T
+    x64 = wl.logits()[1][:T]
+    g64 = wl.grad()[1][:T]
+    bias = wl.bias()
+    b64 = None if bias is None else bias.astype(np.float64)
+    bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
+    out = {}
+    S = M = AS = None
+    for kind in kinds:
+        walls = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            if kind == "topk_fwd":
+                _, M, S, _ = oracle.topk_fwd(x64, wl.K, wl.score_fn, wl.renorm, wl.num_groups,
+                                             wl.group_topk, wl.scaling_factor, b64, threads=thr)
+            elif kind == "topk_bwd":
+                oracle.topk_bwd(g64, S, M, wl.K, wl.score_fn, wl.renorm, wl.scaling_factor,
+                                threads=thr)
+            elif kind == "aux_fwd":
+                _, _, AS = oracle.aux_fwd(x64, wl.K, wl.score_fn, wl.aux_renorm, threads=thr)
+            else:
+                oracle.aux_bwd(g64, AS, wl.score_fn, wl.aux_renorm, threads=thr)
+            walls.append(time.perf_counter() - t0)
+        nb = T * wl.E * bpe[kind] + (wl.E * 4 if (kind == "topk_fwd" and bias is not None)
+                                     else 0)
+        out[kind] = round(nb / float(np.median(walls)) / 1e9, 3)
+    return out
+
+
+SWEEP_ORACLE_TOKENS = 1024
+
+
+def cpu_configs_and_sweep(synth):
+    """The oracle beside the GPU on the five workloads and the E/K sweep
+    (GB/s per pass)."""
+    thr = max(1, min(os.cpu_count() or 1, 64))
+    t0 = time.perf_counter()
+    configs = {}
+    for name, wl in synth.WORKLOADS.items():
+        if wl.T * wl.E > 16384 * 2304:
+            continue
+        kinds = ["topk_fwd", "topk_bwd"] + (["aux_fwd", "aux_bwd"] if wl.aux else [])
+        configs[name] = oracle_gbps(synth, wl, thr, kinds)
+    sweep = {}
+    for sf in (synth.SOFTMAX, synth.SIGMOID):
+        for E in (256, 512, 2304):
+            for K in (4, 8, 22, 36):
+                wl = synth.sweep_workload(E, K, sf)
+                sname = "softmax" if sf == synth.SOFTMAX else "sigmoid"
+                sweep[f"{sname}_{E}x{K}"] = oracle_gbps(
+                    synth, wl, thr, ["topk_fwd", "topk_bwd", "aux_fwd", "aux_bwd"],
+                    T=SWEEP_ORACLE_TOKENS)
+    return {"configs_GBps": configs, "sweep_GBps": sweep, "cores": thr, "kind": "oracle",
+            "sample": f"whole workloads for the configs, the first {SWEEP_ORACLE_TOKENS} of "
+                      f"8192 tokens per sweep cell",
+            "note": f"fp64 C oracle on {thr} host threads, median of 3 runs per pass, same "
+                    f"byte formulas as the GPU figures; {time.perf_counter() - t0:.1f} s"}
+
+
 def cpu_baseline(wl, tokens):
     """The fp64 oracle (as it stands) over the first `tokens` tokens of the
     workload, all four passes, on this host's cores."""
@@ -517,6 +639,7 @@ def main():
     # ---- per-kernel average launch duration: K back-to-back launches of one
     # kind (rotating sets, as in the step), one event pair around them
     per_kernel_us = {}
+    per_launch_us = {}
     timed_kinds = kinds if args.only else step_kinds + LOSS_KINDS
     for kind in timed_kinds:
         k0 = all_kinds.index(kind)
@@ -530,6 +653,15 @@ def main():
         b.record()
         torch.cuda.synchronize()
         per_kernel_us[kind] = a.elapsed_time(b) * 1e3 / args.steps
+        # one event pair per launch: the spread of single launches
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i, (ea, eb) in enumerate(evs):
+            ea.record()
+            launch(kind, sets[(i + k0) % n_sets])
+            eb.record()
+        torch.cuda.synchronize()
+        per_launch_us[kind] = np.array([ea.elapsed_time(eb) * 1e3 for ea, eb in evs])
 
     bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
     kern = {}
@@ -540,9 +672,12 @@ def main():
             nbytes = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None)
                                           else 0)
         avg = per_kernel_us[kind]
+        p10, p50, p90 = np.percentile(per_launch_us[kind], [10, 50, 90])
         kern[kind] = {"us_avg": round(avg, 2), "algo_bytes": nbytes,
                       "GBps": round(nbytes / avg / 1e3, 1),
-                      "frac_of_peak": round(nbytes / avg / 1e3 / PEAK_GBPS, 4)}
+                      "frac_of_peak": round(nbytes / avg / 1e3 / PEAK_GBPS, 4),
+                      "us_single_launch": {"p10": round(p10, 2), "median": round(p50, 2),
+                                           "p90": round(p90, 2)}}
         if args.workload == "c4_softmax_2304x36" and kind in PAGE_B300_GBPS:
             kern[kind]["page_b300_GBps_context"] = PAGE_B300_GBPS[kind]
     step_bytes = sum(k["algo_bytes"] for k in kern.values())
@@ -558,10 +693,13 @@ def main():
     us = sum(kern[k]["us_avg"] for k in by_sym[dom]) / len(by_sym[dom])
     nb = sum(kern[k]["algo_bytes"] for k in by_sym[dom]) / len(by_sym[dom])
     traffic = read_traffic(dom) if args.workload == "c4_softmax_2304x36" and not args.warm else None
+    env = environment(torch, router)
     roof = {"bound": "hbm", "kernel": dom, "passes": by_sym[dom], "us_avg": round(us, 2),
             "achieved": round(nb / us / 1e3, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(nb / us / 1e3 / PEAK_GBPS, 4),
             "algo_bytes_per_launch": int(nb), "traffic": traffic}
+    if args.workload == "c4_softmax_2304x36" and not args.warm:
+        roof["valu"] = valu_busy(read_valu(dom), us, env.get("clock_khz"))
 
     copy = copy_calibration(torch, dev, args.copy_calibration_mib)
 
@@ -586,6 +724,7 @@ def main():
         "kernels": kern,
         "wall_s_timed_region": round(t_wall, 4),
         "device": torch.cuda.get_device_name(0),
+        "environment": env,
         "kernel_source_hash": {"router": kernel_source_hash("fwd_kernel"),
                                "loss": kernel_source_hash("loss_kernel"),
                                "gate": kernel_source_hash("shared_gate_kernel")},
@@ -618,6 +757,8 @@ def main():
         out["copy_calibration"] = copy
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens or T)
+        if not args.only and not args.no_sweep:
+            out["cpu_baseline_configs_sweep"] = cpu_configs_and_sweep(synth)
     if not args.only:
         out["decode_route"] = run_decode_route(torch, router, synth, args.steps)
         out["decode_route_note"] = (

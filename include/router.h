@@ -315,6 +315,16 @@ int router_get_topk_path_threshold(void);
 router_status router_set_topk_path_threshold(int threshold);
 
 /*
+ * Attributes of the current HIP device, for reports next to measured
+ * bandwidth (no passage: bookkeeping of the measurement).  Writes the
+ * compute-unit count, the peak engine clock and the peak memory clock (kHz)
+ * and the memory bus width (bits) through the non-null pointers.
+ * ROUTER_ERR_HIP when no device is usable.
+ */
+router_status router_device_query(int32_t *compute_units, int32_t *clock_khz,
+                                  int32_t *memory_clock_khz, int32_t *memory_bus_bits);
+
+/*
  * Group stage of the group-limited forward.  Passage: the fused-router
  * page, "Forward kernels" (group-limited routing inside the fused kernel).
  * ROUTER_GROUP_STAGE_AUTO (default) scores the groups in registers when

@@ -4,6 +4,7 @@ for gfx950 with hipcc, in-tree next to this file.
 Each kernel translation unit compiles in its own hipcc process, in
 parallel; objects go to _build/ and are linked into one shared library.
 """
+import json
 import os
 import subprocess
 import sys
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librouter.so")
+# what the library was built from and with (written next to it by build())
+BUILD_INFO = os.path.join(HERE, "librouter.build.json")
 ARCH = os.environ.get("ROUTER_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["router_api.cpp", "router_lpt16.hip", "router_lpt32.hip",
@@ -22,7 +25,8 @@ SOURCES = ["router_api.cpp", "router_lpt16.hip", "router_lpt32.hip",
            "router_gate.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-         # packed fp32 VALU forms stay off (see the build notes in DESIGN)
+         # packed fp32 VALU forms (v_pk_*_f32) stay off: hipcc otherwise
+         # forms them by itself from scalar and float2 code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
@@ -53,7 +57,26 @@ def build(jobs=None):
     subprocess.run(["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs,
                     "-o", tmp], check=True)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
+
+
+def _run(cmd):
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=60)
+        return r.stdout.strip() if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def _write_build_info():
+    ver = _run(["hipcc", "--version"])
+    info = {"flags": FLAGS, "sources": SOURCES,
+            "hipcc": ver.splitlines()[0] if ver else None,
+            # the commit the tree was checked out at, "-dirty" with local changes
+            "git": _run(["git", "describe", "--always", "--dirty", "--abbrev=12"])}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
 
 
 if __name__ == "__main__":

@@ -271,7 +271,6 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     p.Kg = G > 0 ? Kg : 0;
     p.q = G > 0 ? K / Kg : 0;
     p.P = G > 0 ? E / G : 0;
-    p.glog = gm == GROUP_REG ? group_reg_log(c, E, G, K / Kg) : 0;
     p.scale = scale;
     const Launch l{grid_for(T, c.lpt), smem, (hipStream_t)stream};
     return launch_fwd(c, dtype, score_fn, gm, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
@@ -578,6 +577,30 @@ router_status router_set_topk_path_threshold(int t)
         return ROUTER_ERR_INVALID_ARG;
     threshold();  // the environment is read first, then overridden
     g_threshold.store(t);
+    return ROUTER_OK;
+}
+
+router_status router_device_query(int32_t *compute_units, int32_t *clock_khz,
+                                  int32_t *memory_clock_khz, int32_t *memory_bus_bits)
+{
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess)
+        return ROUTER_ERR_HIP;
+    const struct {
+        int32_t *out;
+        hipDeviceAttribute_t attr;
+    } q[] = {{compute_units, hipDeviceAttributeMultiprocessorCount},
+             {clock_khz, hipDeviceAttributeClockRate},
+             {memory_clock_khz, hipDeviceAttributeMemoryClockRate},
+             {memory_bus_bits, hipDeviceAttributeMemoryBusWidth}};
+    for (const auto &e : q) {
+        if (!e.out)
+            continue;
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, e.attr, d) != hipSuccess)
+            return ROUTER_ERR_HIP;
+        *e.out = (int32_t)v;
+    }
     return ROUTER_OK;
 }
 

@@ -568,8 +568,9 @@ __device__ __forceinline__ void group_limit_reg_t(float (&key)[NCH][4],
     }
 }
 
-// Dispatch on the lanes per group (p.glog) and the list length; the host
-// takes this stage only for the combinations built here (group_reg_ok).
+// Dispatch on the lanes per group (P / 4, a power of two here) and the
+// list length; the host takes this stage only for the combinations built
+// here (group_reg_ok).
 template <int LPT, int NCH>
 __device__ __forceinline__ void group_limit_reg(float (&key)[NCH][4], const float (&s)[NCH][4],
                                                 bool has_bias, const FwdParams &p, int lane)
@@ -583,7 +584,7 @@ __device__ __forceinline__ void group_limit_reg(float (&key)[NCH][4], const floa
                 group_limit_reg_t<LPT, NCH, LG, 4>(key, s, has_bias, p, lane);
         }
     };
-    switch (p.glog) {
+    switch (__builtin_ctz((unsigned)p.P) - 2) {
     case 0: run(std::integral_constant<int, 0>{}); break;
     case 1: run(std::integral_constant<int, 1>{}); break;
     case 2: run(std::integral_constant<int, 2>{}); break;

@@ -47,8 +47,7 @@ struct FwdParams {
     int G;                // groups (0 = none)
     int Kg;               // groups kept
     int q;                // K / Kg
-    int P;                // E / G
-    int glog;             // GROUP_REG: log2 of the lanes per group (P / 4)
+    int P;                // E / G (GROUP_REG: 4 * 2^k for 2^k lanes per group)
     float scale;          // scaling factor (topk)
 };
 

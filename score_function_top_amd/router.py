@@ -75,6 +75,8 @@ def load():
     lib.router_set_topk_path_threshold.argtypes = [ci]
     lib.router_get_topk_path_threshold.argtypes = []
     lib.router_get_topk_path_threshold.restype = ci
+    lib.router_device_query.argtypes = [vp, vp, vp, vp]
+    lib.router_device_query.restype = ci
     lib.router_set_group_stage.argtypes = [ci]
     lib.router_set_group_stage.restype = ci
     lib.router_get_group_stage.argtypes = []
@@ -100,6 +102,15 @@ def set_topk_path_threshold(threshold):
 
 def get_topk_path_threshold():
     return load().router_get_topk_path_threshold()
+
+
+def device_query():
+    """Attributes of the current device: compute units, peak engine and
+    memory clocks (kHz), memory bus width (bits)."""
+    vals = [ctypes.c_int32() for _ in range(4)]
+    check(load().router_device_query(*[ctypes.byref(v) for v in vals]))
+    return dict(zip(("compute_units", "clock_khz", "memory_clock_khz", "memory_bus_bits"),
+                    (v.value for v in vals)))
 
 
 GROUP_STAGE_AUTO = 0

@@ -125,6 +125,15 @@ def test_threshold_setter():
         router.set_topk_path_threshold(old)
 
 
+def test_device_query_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present (covered by the GPU tests)")
+    with pytest.raises(router.RouterError) as e:
+        router.device_query()
+    assert e.value.status == router.ERR_HIP
+
+
 def test_group_stage_setter():
     assert router.get_group_stage() == router.GROUP_STAGE_AUTO
     try:

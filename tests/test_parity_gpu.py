@@ -404,6 +404,13 @@ def test_zero_tokens():
     assert da.shape == (0, 64)
 
 
+def test_device_query():
+    q = router.device_query()
+    props = torch.cuda.get_device_properties(0)
+    assert q["compute_units"] == props.multi_processor_count
+    assert q["clock_khz"] > 0 and q["memory_clock_khz"] > 0 and q["memory_bus_bits"] > 0
+
+
 def test_side_stream():
     wl = WL["c2_softmax_256x4"]
     x_st, x64 = wl.logits()

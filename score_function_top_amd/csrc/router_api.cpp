@@ -149,7 +149,7 @@ int widen(int lpt, int need) { return need <= lpt ? lpt : (need <= 32 ? 32 : 64)
 // log2 of the lanes per group when the register group stage can take G
 // groups of E/G experts in the layout c with q = K/Kg summed per group:
 // E/G = 4*L with L a power of two no larger than the lane width, at most
-// kGroupRegSlots group slots, a vector kernel of at most kGroupRegMaxNch
+// group_reg_slots(nch) group slots, a vector kernel of at most kGroupRegMaxNch
 // chunks, q <= 4.  -1 otherwise.
 int group_reg_log(const Cfg &c, int E, int G, int q)
 {

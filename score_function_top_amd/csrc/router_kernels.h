@@ -146,6 +146,13 @@ __device__ __forceinline__ float tree_sum(const float *v)
     }
 }
 
+// IEEE maximum / minimum (v_maximum3 / v_minimum3 on gfx950): unlike
+// fmaxf / fminf they need no canonicalisation of their inputs, and they
+// agree with them on every value used here (never NaN; where -0 can occur
+// the result feeds only comparisons or a +0 canonicalisation).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
 // ------------------------------------------------------------ selection
 //
 // Selection keys are floats: the logit without a bias, fp32(s + b) with
@@ -428,25 +435,26 @@ __device__ __forceinline__ void group_limit(float (&key)[NCH][4], const FwdParam
 //
 // Merge of two descending lists a, b of length Q into the Q largest of
 // both, descending: max(a_i, b_{Q-1-i}) holds exactly those values in a
-// V-shaped order, which one bitonic pass sorts.
+// V-shaped order, which one bitonic pass sorts.  Group values are never
+// NaN and never -0 (s >= +0, and s + b rounds an exact zero to +0).
 template <int Q>
 __device__ __forceinline__ void topq_merge(float (&a)[Q], const float (&b)[Q])
 {
     float c[Q];
 #pragma unroll
     for (int i = 0; i < Q; i++)
-        c[i] = fmaxf(a[i], b[Q - 1 - i]);
+        c[i] = vmax(a[i], b[Q - 1 - i]);
     if constexpr (Q == 2) {
-        a[0] = fmaxf(c[0], c[1]);
-        a[1] = fminf(c[0], c[1]);
+        a[0] = vmax(c[0], c[1]);
+        a[1] = vmin(c[0], c[1]);
     } else {
         static_assert(Q == 4, "lists of 2 or 4");
-        const float h0 = fmaxf(c[0], c[2]), l0 = fminf(c[0], c[2]);
-        const float h1 = fmaxf(c[1], c[3]), l1 = fminf(c[1], c[3]);
-        a[0] = fmaxf(h0, h1);
-        a[1] = fminf(h0, h1);
-        a[2] = fmaxf(l0, l1);
-        a[3] = fminf(l0, l1);
+        const float h0 = vmax(c[0], c[2]), l0 = vmin(c[0], c[2]);
+        const float h1 = vmax(c[1], c[3]), l1 = vmin(c[1], c[3]);
+        a[0] = vmax(h0, h1);
+        a[1] = vmin(h0, h1);
+        a[2] = vmax(l0, l1);
+        a[3] = vmin(l0, l1);
     }
 }
 
@@ -454,18 +462,18 @@ __device__ __forceinline__ void topq_merge(float (&a)[Q], const float (&b)[Q])
 template <int Q>
 __device__ __forceinline__ void topq_of4(const float (&x)[4], float (&t)[Q])
 {
-    const float a = fmaxf(x[0], x[1]), b = fminf(x[0], x[1]);
-    const float c = fmaxf(x[2], x[3]), d = fminf(x[2], x[3]);
+    const float a = vmax(x[0], x[1]), b = vmin(x[0], x[1]);
+    const float c = vmax(x[2], x[3]), d = vmin(x[2], x[3]);
     if constexpr (Q == 2) {
-        t[0] = fmaxf(a, c);
-        t[1] = fmaxf(fminf(a, c), fmaxf(b, d));
+        t[0] = vmax(a, c);
+        t[1] = vmax(vmin(a, c), vmax(b, d));
     } else {
         static_assert(Q == 4, "lists of 2 or 4");
-        t[0] = fmaxf(a, c);
-        t[3] = fminf(b, d);
-        const float m1 = fminf(a, c), m2 = fmaxf(b, d);
-        t[1] = fmaxf(m1, m2);
-        t[2] = fminf(m1, m2);
+        t[0] = vmax(a, c);
+        t[3] = vmin(b, d);
+        const float m1 = vmin(a, c), m2 = vmax(b, d);
+        t[1] = vmax(m1, m2);
+        t[2] = vmin(m1, m2);
     }
 }
 
@@ -648,7 +656,7 @@ fwd_kernel(FwdParams p)
             for (int c = 0; c < NCH; c++)
 #pragma unroll
                 for (int u = 0; u < 4; u++)
-                    m = fmaxf(m, key[c][u]);
+                    m = vmax(m, key[c][u]);  // logits: finite, or -inf padding
             mx = group_max<LPT>(m);
             mx = tok ? mx : 0.0f;
         }

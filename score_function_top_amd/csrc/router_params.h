@@ -19,16 +19,17 @@ enum { SCORE_SOFTMAX = 0, SCORE_SIGMOID = 1 };
 // so each lane's four elements of a chunk share one group).
 enum { GROUP_NONE = 0, GROUP_LDS = 1, GROUP_REG = 2 };
 
-// Register group stage: at most this many group slots (chunks times groups
-// per chunk) per token, and chunk counts it is built for.
-constexpr int kGroupRegSlots = 16;
+// Register group stage: chunk counts it is built for, and the group slots
+// (chunks times groups per chunk) it holds per token: 16 up to two chunks,
+// 8 from three on (16 slots there push the prune kernels past 128 VGPRs).
 constexpr int kGroupRegMaxNch = 4;
+constexpr int group_reg_slots(int nch) { return nch >= 3 ? 8 : 16; }
 // Built (lanes per token LPT, chunks NCH, log2 of lanes per group LG):
-// L = 2^LG <= LPT and NCH * LPT / L <= kGroupRegSlots group slots.
+// L = 2^LG <= LPT and NCH * LPT / L <= group_reg_slots(NCH).
 constexpr bool group_reg_ok(int lpt, int nch, int lg)
 {
     return nch <= kGroupRegMaxNch && lg >= 0 && (1 << lg) <= lpt &&
-           nch * (lpt >> lg) <= kGroupRegSlots;
+           nch * (lpt >> lg) <= group_reg_slots(nch);
 }
 
 struct FwdParams {

@@ -199,14 +199,16 @@ def test_grouped_softmax():
 
 
 # Shapes the register group stage takes (4*L experts per group, L a power of
-# two up to the lanes per token, at most 16 group slots, q <= 4).
+# two up to the lanes per token, at most 16 group slots (8 from three chunks
+# on), q <= 4).
 GROUP_STAGE_CASES = [
     (500, 256, 8, 8, 4, synth.BF16, synth.SIGMOID, 0.05),   # 8 lanes per group, q = 2
     (257, 256, 16, 8, 4, synth.BF16, synth.SIGMOID, 0.0),   # q = 4
     (200, 64, 6, 4, 2, synth.F32, synth.SIGMOID, 0.05),     # 4 lanes, one chunk
     (90, 96, 12, 12, 4, synth.F32, synth.SIGMOID, 0.0),     # 2 lanes, q = 3, 16 slots
-    (70, 160, 9, 10, 3, synth.F32, synth.SOFTMAX, 0.0),     # slots past E
-    (129, 512, 22, 16, 11, synth.F32, synth.SIGMOID, 0.05), # 32-lane tokens
+    (70, 192, 6, 6, 3, synth.F32, synth.SOFTMAX, 0.0),      # slots past E
+    (70, 160, 9, 10, 3, synth.F32, synth.SOFTMAX, 0.0),     # 16 slots at 4 chunks: LDS
+    (129, 512, 12, 8, 4, synth.F32, synth.SIGMOID, 0.05),   # 32-lane tokens, q = 3
     (100, 512, 16, 4, 4, synth.F32, synth.SIGMOID, 0.0),    # a group fills a chunk
     (64, 1024, 8, 8, 4, synth.F32, synth.SIGMOID, 0.05),    # 64-lane tokens
     (65, 768, 12, 6, 3, synth.BF16, synth.SOFTMAX, 0.0),    # three chunks

@@ -127,7 +127,22 @@ int pick_nch(const int (&list)[N], int need)
     return -1;
 }
 
-int lpt_for_rows(int E) { return E <= 256 ? 16 : (E <= 512 ? 32 : 64); }
+// Lanes per token for rows of E experts: the row in at most 4 chunks of
+// 4 elements per lane, except that rows of 129..256 experts take 32 lanes
+// (two chunks) when T is small enough that 16-lane tokens leave the SIMDs
+// with few waves: T <= 8192, or T <= 16384 with the group stage, whose
+// per-token work is larger.  Measured on MI355X (fp32 softmax K=4 at
+// T=8192: forward 8.1 -> 7.1 us, backward 7.4 -> 6.4 us; grouped bf16
+// sigmoid at T=16384: 18.7 -> 15.8 us; the 16-lane form stays ahead at
+// T=65536 and without groups at T=16384).
+int lpt_for_rows(int E, int64_t T, bool grouped)
+{
+    if (E <= 128)
+        return 16;
+    if (E <= 256)
+        return T <= 8192 || (grouped && T <= 16384) ? 32 : 16;
+    return E <= 512 ? 32 : 64;
+}
 
 // Fills nch for c.lpt / c.vec; false when no built kernel holds E.
 bool fill_nch(Cfg &c, int E)
@@ -231,7 +246,7 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
                      aligned(map, 16) && (!bias || aligned(bias, 16));
     const int thr = threshold();
     int sel = K < thr ? SEL_ARGMAX : SEL_PRUNE;
-    Cfg c{vec ? lpt_for_rows(E) : 64, 0, vec};
+    Cfg c{vec ? lpt_for_rows(E, T, G > 0) : 64, 0, vec};
     if (sel == SEL_PRUNE)
         c.lpt = widen(c.lpt, K);
     if (G > 0)
@@ -297,7 +312,7 @@ router_status bwd_common(const void *g, const float *s, const uint8_t *m, int dt
         return ROUTER_ERR_INVALID_ARG;
     const bool vec = E % 4 == 0 && aligned(g, 16) && aligned(dx, 16) && aligned(s, 16) &&
                      (aux || aligned(m, 16));
-    Cfg c{vec ? lpt_for_rows(E) : 64, 0, vec};
+    Cfg c{vec ? lpt_for_rows(E, T, false) : 64, 0, vec};
     if (!fill_nch(c, E))
         return ROUTER_ERR_UNSUPPORTED;
     DevInfo dev;

@@ -212,6 +212,8 @@ GROUP_STAGE_CASES = [
     (100, 512, 16, 4, 4, synth.F32, synth.SIGMOID, 0.0),    # a group fills a chunk
     (64, 1024, 8, 8, 4, synth.F32, synth.SIGMOID, 0.05),    # 64-lane tokens
     (65, 768, 12, 6, 3, synth.BF16, synth.SOFTMAX, 0.0),    # three chunks
+    (100, 64, 8, 16, 8, synth.F32, synth.SIGMOID, 0.05),    # 1 lane per group, 16 slots, q = 1
+    (80, 1024, 4, 4, 2, synth.BF16, synth.SOFTMAX, 0.0),    # 64 lanes per group
 ]
 
 

@@ -610,7 +610,8 @@ __device__ __forceinline__ void group_limit_reg(float (&key)[NCH][4], const floa
 // group-limited routing (p.G > 0): GROUP_NONE, GROUP_LDS (group_limit, any
 // P) or GROUP_REG (group_limit_reg, groups that tile the chunks).
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC>
-__global__ void __launch_bounds__(kBlock, GM == GROUP_LDS && VEC && NCH <= 4 ? 3 : (GM == GROUP_REG ? 4 : 1))
+__global__ void __launch_bounds__(kBlock, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
+                                                 : (GM == GROUP_REG ? (NCH <= 2 ? 5 : 4) : 1))
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave

@@ -194,6 +194,49 @@ def test_groups(T, E, K, G, Kg, dtype, biased):
     run_fwd(wl)
 
 
+def _random_cases(n=48, seed=2024):
+    """Seeded random router configurations around the size boundaries of
+    the launch plans (lanes per token, chunk counts, selection paths, both
+    group stages)."""
+    rng = np.random.default_rng(seed)
+    edges = [(1, 16), (60, 70), (125, 135), (250, 260), (500, 520), (1000, 1030),
+             (2300, 2310), (4090, 4096)]
+    out = []
+    while len(out) < n:
+        lo, hi = edges[rng.integers(len(edges))]
+        E = int(rng.integers(lo, hi + 1))
+        T = int(rng.choice([1, 3, 17, 64, 129, 300, 513, 700, 8193]))
+        sf = int(rng.integers(2))
+        G = Kg = 0
+        divs = [d for d in range(2, 65) if E % d == 0]
+        if divs and rng.random() < 0.4:
+            G = int(rng.choice(divs))
+            Kg = int(rng.integers(1, G + 1))
+            q = int(rng.integers(1, min(6, E // G) + 1))
+            K = Kg * q
+        else:
+            K = int(rng.integers(1, min(E, 80) + 1))
+        bias = 0.05 if sf == synth.SIGMOID and rng.random() < 0.5 else 0.0
+        dtype = synth.BF16 if rng.random() < 0.3 else synth.F32
+        renorm = bool(rng.integers(2))
+        out.append((T, E, K, sf, renorm, bias, G, Kg, dtype, int(rng.integers(1 << 20))))
+    return out
+
+
+@pytest.mark.parametrize("T,E,K,sf,renorm,b,G,Kg,dtype,seed", _random_cases())
+def test_random_configs(T, E, K, sf, renorm, b, G, Kg, dtype, seed):
+    """Forward and backward against the oracle on seeded random shapes."""
+    wl = edge_wl(T, E, K, sf, renorm, bias=b, G=G, Kg=Kg, dtype=dtype, c=1.25, seed=seed)
+    r = run_fwd(wl)
+    g_st, g64 = grads(wl, T)
+    dx = router.router_topk_bwd(to_dev(g_st, dtype), r["inter"], r["map"], K,
+                                SCORE_NAME[sf], renorm, 1.25)
+    torch.cuda.synchronize()
+    ref = oracle.topk_bwd(g64, r["S"], r["M"], K, sf, renorm, 1.25, threads=threads())
+    ext = chain_tol(g64, r["S"], r["M"], K, sf, renorm, 1.25)
+    assert_close(f64(dx), ref, dtype, f"{wl.name} grad", extra=ext)
+
+
 def test_grouped_softmax():
     run_fwd(edge_wl(300, 256, 8, synth.SOFTMAX, True, G=8, Kg=4, seed=13))
 

@@ -11,8 +11,8 @@
 // Lane l of a group holds NCH chunks of 4 consecutive elements: element
 // j = c*4*LPT + 4*l + u for chunk c and component u, so every chunk load
 // or store of a group is one contiguous segment.  The whole row lives in
-// VGPRs; LDS holds only a 2*LPT candidate list per token (and, for grouped
-// routing, the row's group values).
+// VGPRs; LDS holds only a 3*LPT-slot candidate list per token (and, for the
+// LDS form of group-limited routing, the row's group values).
 //
 // Selection of the K largest keys (ties to the lower index) is exact and
 // reduces to one 64-bit threshold: with pack(j) = key_j << 32 | ~j (unique
@@ -28,8 +28,8 @@
 //           2*LPT candidates, or when K > LPT).
 //
 // Code shape: no branch depends on a single element.  Padding is encoded in
-// the data (key 0, score 0); stores of masked chunks get a byte offset past
-// the buffer's range, which the hardware drops.
+// the data (key -inf, score 0); stores of masked chunks get a byte offset
+// past the buffer's range, which the hardware drops.
 #pragma once
 
 #include <type_traits>

@@ -64,8 +64,8 @@ struct BwdParams {
     float scale;
 };
 
-// LDS per token group: cand_slots u64 candidate slots; grouped routing adds
-// group_scratch_floats floats.
+// LDS per token group: cand_slots u64 candidate slots; the LDS group stage
+// adds group_scratch_floats floats.
 constexpr int cand_slots(int lpt) { return 3 * lpt; }
 constexpr int group_scratch_floats(int E, int G, int lpt)
 {

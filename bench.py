@@ -716,6 +716,15 @@ def main():
             "algo_bytes_per_launch": int(nb), "traffic": traffic}
     if args.workload == "c4_softmax_2304x36" and not args.warm:
         roof["valu"] = valu_busy(read_valu(dom), us, env.get("clock_khz"))
+        # the committed counter summaries of every pass's kernel, where they
+        # match the current sources
+        for kind in kinds:
+            if kind in LOSS_KINDS:
+                continue
+            sym = KERNEL_SYMBOL[kind]
+            kern[kind]["traffic"] = read_traffic(sym)
+            kern[kind]["valu"] = valu_busy(read_valu(sym), kern[kind]["us_avg"],
+                                           env.get("clock_khz"))
 
     copy = copy_calibration(torch, dev, args.copy_calibration_mib)
 

@@ -611,7 +611,7 @@ __device__ __forceinline__ void group_limit_reg(float (&key)[NCH][4], const floa
 // P) or GROUP_REG (group_limit_reg, groups that tile the chunks).
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC>
 __global__ void __launch_bounds__(kBlock, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
-                                                 : (GM == GROUP_REG ? (NCH <= 2 ? 5 : 4) : 1))
+                                                 : (GM == GROUP_REG ? (NCH <= 2 && LPT >= 32 ? 5 : 4) : 1))
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave
@@ -706,6 +706,18 @@ fwd_kernel(FwdParams p)
                 }
             }
         }
+
+        // ---- the intermediate is final: store it now, so its writes overlap
+        // the selection work (no global load follows in this iteration, so
+        // no wait on the memory counter covers these stores; ~6% at E=2304).
+        // Probs and map wait for the selection: storing the chunks known to
+        // be zero early splits cache lines between two write bursts, which
+        // measured 1.7x slower.
+        const rsrc_t ri = make_rsrc(p.inter + off0, nel * 4u);
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+            store_chunk<LPT, float, VEC>(ri, goff, c, j_lane, E, s[c]);
+
         if constexpr (GM == GROUP_LDS)
             group_limit<LPT, NCH>(key, p, lane, j_lane, tok, invP, gscr);
         if constexpr (GM == GROUP_REG)
@@ -779,7 +791,6 @@ fwd_kernel(FwdParams p)
 
         // ---- stores (tokens past T fall outside the buffers and are dropped)
         const rsrc_t ro = make_rsrc(static_cast<TIn *>(p.out) + off0, nel * io<TIn>::kSize);
-        const rsrc_t ri = make_rsrc(p.inter + off0, nel * 4u);
         const rsrc_t rm = make_rsrc(p.map + off0, nel);
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
@@ -788,7 +799,6 @@ fwd_kernel(FwdParams p)
 #pragma unroll
             for (int u = 0; u < 4; u++)
                 o[u] = ((kw >> (8 * u)) & 0xFFu) ? s[c][u] * mult : 0.0f;
-            store_chunk<LPT, float, VEC>(ri, goff, c, j_lane, E, s[c]);
             store_chunk<LPT, TIn, VEC>(ro, goff, c, j_lane, E, o);
             store_map_chunk<LPT, VEC>(rm, goff, c, j_lane, E, mw[c]);
         }

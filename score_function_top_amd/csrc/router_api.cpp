@@ -470,7 +470,7 @@ router_status router_aux_loss_bwd(const float *grad_loss, const int64_t *tokens_
         return ROUTER_ERR_INVALID_ARG;
     const bool vec = E % 4 == 0 && aligned(grad_scores, 4 * ds);
     const hipError_t e = launch_loss_bwd(grad_loss, tokens_per_expert, dtype, vec,
-                                         loss_geo(T, E), loss_coeff(coeff, E, total_tokens, K),
+                                         loss_bwd_geo(T, E), loss_coeff(coeff, E, total_tokens, K),
                                          grad_scores, (hipStream_t)hip_stream);
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kBlock) void loss_bwd_kernel(const float *grad_loss
     for (int64_t sp = s0; sp < g.nsplit; sp += g.gsplit) {
         const rsrc_t r = split_rsrc(dx, g, sp, sz);
 #pragma unroll
-        for (int k = 0; k < kLossSteps; k++) {
+        for (int k = 0; k < kLossBwdSteps; k++) {
             const uint32_t e =
                 (uint32_t)split_row(g, w, k, lc.row_lane) * (uint32_t)g.E + (uint32_t)lc.col0;
             if constexpr (VEC) {

@@ -5,7 +5,8 @@
 // other access is masked (column >= E) or past its split's buffer, that
 // byte offsets fit the 32-bit buffer offsets, that the LDS column index of
 // the count kernel stays within its array, and that the loss workspace fits
-// the queried size.  Prints "ok" or the first failure; exit status 0/1.
+// the queried size (the forward's geometry; the gradient's writes only).
+// Prints "ok" or the first failure; exit status 0/1.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -107,6 +108,8 @@ int main()
             bad |= check(T, E, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks, 1);
             bad |= check(T, E, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks, 4);
             bad |= check(T, E, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks, 2);
+            bad |= check(T, E, kLossWaves, kLossCpl, kLossBwdSteps, kLossBwdMaxBlocks, 4);
+            bad |= check(T, E, kLossWaves, kLossCpl, kLossBwdSteps, kLossBwdMaxBlocks, 2);
             if (bad)
                 return 1;
         }
@@ -115,6 +118,7 @@ int main()
     bad |= check(40000, 2304, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks, 1);
     bad |= check(70000, 2304, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks, 4);
     bad |= check(100000, 4, kLossWaves, kLossCpl, kLossSteps, 64, 4);
+    bad |= check(40000, 2304, kLossWaves, kLossCpl, kLossBwdSteps, kLossBwdMaxBlocks, 4);
     if (bad)
         return 1;
     std::printf("ok\n");

@@ -73,6 +73,14 @@ SYMBOL_SOURCES = {"fwd_kernel": _ROUTER_SOURCES, "bwd_kernel": _ROUTER_SOURCES,
                   "loss_bwd_kernel": _LOSS_SOURCES, "shared_gate_kernel": _GATE_SOURCES}
 
 
+def path_threshold_desc(router):
+    """The top-k path setting as reported in the JSON line."""
+    t = router.get_topk_path_threshold()
+    if t == router.TOPK_PATH_AUTO:
+        return "auto (argmax rounds for K < 5 / 4 / 2 at <= 4 / <= 8 / more elements per lane)"
+    return t
+
+
 def kernel_source_hash(symbol="fwd_kernel"):
     h = hashlib.sha256()
     for name in sorted(SYMBOL_SOURCES[symbol]):
@@ -744,7 +752,7 @@ def main():
                    "cache": "warm (one buffer set)" if args.warm else
                             f"cold ({n_sets} rotating buffer sets, "
                             f"{n_sets * set_bytes / 2**30:.2f} GiB)",
-                   "path_threshold": router.get_topk_path_threshold()},
+                   "path_threshold": path_threshold_desc(router)},
         "roofline": roof,
         "kernels": kern,
         "wall_s_timed_region": round(t_wall, 4),

@@ -305,12 +305,20 @@ const char *router_status_str(router_status s);
  * K below the threshold selects by K rounds of a lane-group argmax; K at or
  * above it selects through a pruned candidate sort (an exact bit-wise
  * search when K exceeds the lanes per token or the pruning leaves too many
- * candidates).  Every path returns the same map.  The threshold is read
- * once from the environment variable ROUTER_TOPK_PATH_THRESHOLD (default
- * 8; a value that is not an integer in [0, 4096] keeps the default) and can
- * be overridden with router_set_topk_path_threshold, which rejects values
- * outside [0, 4096] with ROUTER_ERR_INVALID_ARG.
+ * candidates).  Every path returns the same map.
+ * ROUTER_TOPK_PATH_AUTO (the default) picks the crossover from the row
+ * layout: with e elements of a row per lane, the argmax rounds run for
+ * K < 5 when e <= 4, K < 4 when e <= 8 and K < 2 otherwise (where the
+ * rounds measured slower than the pruned sort on MI355X).  A value in
+ * [0, 4096] fixes the crossover for every shape.  The setting is read once
+ * from the environment variable ROUTER_TOPK_PATH_THRESHOLD (an integer in
+ * [0, 4096]; anything else, or no variable, means auto) and can be
+ * overridden with router_set_topk_path_threshold, which takes
+ * ROUTER_TOPK_PATH_AUTO or [0, 4096] and rejects other values with
+ * ROUTER_ERR_INVALID_ARG.  router_get_topk_path_threshold returns the
+ * setting (ROUTER_TOPK_PATH_AUTO in auto mode).
  */
+#define ROUTER_TOPK_PATH_AUTO (-1)
 int router_get_topk_path_threshold(void);
 router_status router_set_topk_path_threshold(int threshold);
 

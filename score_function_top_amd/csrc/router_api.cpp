@@ -7,7 +7,7 @@
 // element count that cannot overflow the index arithmetic (here 64-bit
 // offsets, so the bound is the 64-bit byte count).  The top-k path
 // threshold mirrors that page's crossover variable ("Simple kernel path for
-// small topk"; default 8).
+// small topk"); by default the crossover follows the row layout.
 #include "router.h"
 
 #include <hip/hip_runtime_api.h>
@@ -26,14 +26,15 @@ namespace {
 
 // ------------------------------------------------------------ threshold
 
-constexpr int kDefaultThreshold = 8;
-std::atomic<int> g_threshold{-1};
+constexpr int kUnread = -2;  // the environment has not been read yet
+std::atomic<int> g_threshold{kUnread};
 std::once_flag g_threshold_once;
 
+// ROUTER_TOPK_PATH_AUTO or a fixed crossover in [0, ROUTER_MAX_EXPERTS].
 int threshold()
 {
     std::call_once(g_threshold_once, [] {
-        int v = kDefaultThreshold;
+        int v = ROUTER_TOPK_PATH_AUTO;
         if (const char *e = std::getenv("ROUTER_TOPK_PATH_THRESHOLD")) {
             char *end = nullptr;
             errno = 0;
@@ -41,11 +42,20 @@ int threshold()
             if (errno == 0 && end != e && *end == '\0' && x >= 0 && x <= ROUTER_MAX_EXPERTS)
                 v = (int)x;
         }
-        int expect = -1;
+        int expect = kUnread;
         g_threshold.compare_exchange_strong(expect, v);
     });
     return g_threshold.load();
 }
+
+// Automatic crossover for rows held as `epl` elements per lane: the
+// argmax rounds cost about a pass over the lane's elements each, the
+// pruned sort a fixed number of cross-lane stages, so the rounds stop
+// paying sooner on longer lanes.  Measured on MI355X at T=8192 (graph
+// replay, cold): the sort is ahead from K=5 at 4 elements per lane (E=16,
+// 64), from K=4 at 8 (E=128, 256: 6.97 -> 6.44 us at E=256, K=4) and from
+// K=2 at 16 or more (E=512: 10.25 -> 9.73 us; E=2304: 47.6 -> 44.5 us).
+int auto_threshold(int epl) { return epl <= 4 ? 5 : (epl <= 8 ? 4 : 2); }
 
 std::atomic<int> g_group_stage{ROUTER_GROUP_STAGE_AUTO};
 
@@ -244,9 +254,15 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
 
     const bool vec = E % 4 == 0 && aligned(x, 16) && aligned(out, 16) && aligned(inter, 16) &&
                      aligned(map, 16) && (!bias || aligned(bias, 16));
-    const int thr = threshold();
-    int sel = K < thr ? SEL_ARGMAX : SEL_PRUNE;
     Cfg c{vec ? lpt_for_rows(E, T, G > 0) : 64, 0, vec};
+    int thr = threshold();
+    if (thr == ROUTER_TOPK_PATH_AUTO) {
+        Cfg a = c;
+        if (!fill_nch(a, E))
+            return ROUTER_ERR_UNSUPPORTED;
+        thr = auto_threshold(4 * a.nch);
+    }
+    int sel = K < thr ? SEL_ARGMAX : SEL_PRUNE;
     if (sel == SEL_PRUNE)
         c.lpt = widen(c.lpt, K);
     if (G > 0)
@@ -588,7 +604,7 @@ int router_get_topk_path_threshold(void) { return threshold(); }
 
 router_status router_set_topk_path_threshold(int t)
 {
-    if (t < 0 || t > ROUTER_MAX_EXPERTS)
+    if ((t < 0 && t != ROUTER_TOPK_PATH_AUTO) || t > ROUTER_MAX_EXPERTS)
         return ROUTER_ERR_INVALID_ARG;
     threshold();  // the environment is read first, then overridden
     g_threshold.store(t);

@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
                     acc = dot16<TIn>(hpre[c], gv, acc);
                 }
                 const float logit = group_sum<64>(acc);
-                gate = lane == K + s ? p.scale * sigmoid_fast(logit) : gate;
+                // every lane evaluates it: no lane-divergent branch
+                const float sg = p.scale * sigmoid_fast(logit);
+                gate = lane == K + s ? sg : gate;
             }
             store_row(p, m, lane, id, wt, gate);
             continue;
@@ -167,7 +169,8 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
         for (int s = 0; s < kGateMaxShared; s++) {
             if (s < S) {
                 const float logit = group_sum<64>(acc[s]);
-                gate = lane == K + s ? p.scale * sigmoid_fast(logit) : gate;
+                const float sg = p.scale * sigmoid_fast(logit);
+                gate = lane == K + s ? sg : gate;
             }
         }
 

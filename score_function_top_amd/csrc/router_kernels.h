@@ -661,18 +661,35 @@ fwd_kernel(FwdParams p)
             mx = group_max<LPT>(m);
             mx = tok ? mx : 0.0f;
         }
+        // Sigmoid on padding (key -inf): the vector kernels skip it with a
+        // branch (about 3% faster at E = 512 and 2304 than computing and
+        // dropping it).  The element-wise kernels compute it on every element
+        // and select: there the branch led hipcc to place a register copy of
+        // another element's score in the join block ahead of the exec
+        // restore (16-chunk forward), so lanes with padding kept a stale
+        // value.  A code-generation test rejects that pattern in every kernel.
 #pragma unroll
         for (int c = 0; c < NCH; c++)
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                if constexpr (SCORE == SCORE_SOFTMAX)
+                if constexpr (SCORE == SCORE_SOFTMAX) {
                     s[c][u] = exp_split(key[c][u] - mx);           // padding: exactly 0
-                else
-                    s[c][u] = key[c][u] == -INFINITY ? 0.0f : sigmoid_fast(key[c][u]);
+                } else {
+                    if constexpr (VEC) {
+                        s[c][u] = key[c][u] == -INFINITY ? 0.0f : sigmoid_fast(key[c][u]);
+                    } else {
+                        const float sg = sigmoid_fast(key[c][u]);
+                        s[c][u] = key[c][u] == -INFINITY ? 0.0f : sg;
+                    }
+                }
             }
         if constexpr (SCORE == SCORE_SOFTMAX) {
             const float z = group_sum<LPT>(tree_sum<VPL>(&s[0][0]));
-            const float rz = tok ? 1.0f / z : 0.0f;
+            // the divisions here run on every lane (idle groups divide by
+            // 0 and the select drops the result): kept out of lane-divergent
+            // branches, like the sigmoid above
+            const float rz0 = 1.0f / z;
+            const float rz = tok ? rz0 : 0.0f;
 #pragma unroll
             for (int c = 0; c < NCH; c++)
 #pragma unroll
@@ -786,7 +803,8 @@ fwd_kernel(FwdParams p)
                 part[c] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
             }
             const float a = group_sum<LPT>(tree_sum<NCH>(part));
-            mult = tok ? mult / a : 0.0f;
+            const float mq = mult / a;
+            mult = tok ? mq : 0.0f;
         }
 
         // ---- stores (tokens past T fall outside the buffers and are dropped)
@@ -885,7 +903,8 @@ bwd_kernel(BwdParams p)
         }
         float alpha = c0, beta = SCORE == SCORE_SOFTMAX ? B : 0.0f;
         if (renorm_mode) {
-            const float rA = Ev ? 1.0f / A : 0.0f;
+            const float rA0 = 1.0f / A;  // every lane: no divergent branch
+            const float rA = Ev ? rA0 : 0.0f;
             alpha = c0 * rA;
             beta = B * rA;
         }

@@ -96,6 +96,9 @@ def check(status):
         raise RouterError(status, status_str(status))
 
 
+TOPK_PATH_AUTO = -1  # crossover chosen from the row layout (the default)
+
+
 def set_topk_path_threshold(threshold):
     check(load().router_set_topk_path_threshold(int(threshold)))
 

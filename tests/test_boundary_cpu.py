@@ -117,7 +117,9 @@ def test_threshold_setter():
         assert router.get_topk_path_threshold() == 0
         router.set_topk_path_threshold(64)
         assert router.get_topk_path_threshold() == 64
-        for bad in (-1, 4097):
+        router.set_topk_path_threshold(router.TOPK_PATH_AUTO)
+        assert router.get_topk_path_threshold() == router.TOPK_PATH_AUTO
+        for bad in (-2, -100, 4097):
             with pytest.raises(router.RouterError) as e:
                 router.set_topk_path_threshold(bad)
             assert e.value.status == INV
@@ -148,8 +150,9 @@ def test_group_stage_setter():
         router.set_group_stage(router.GROUP_STAGE_AUTO)
 
 
-@pytest.mark.parametrize("env,expect", [(None, 8), ("3", 3), ("0", 0), ("abc", 8),
-                                        ("-4", 8), ("5000", 8), ("12x", 8)])
+@pytest.mark.parametrize("env,expect", [(None, -1), ("3", 3), ("0", 0), ("8", 8),
+                                        ("4096", 4096), ("abc", -1), ("-4", -1),
+                                        ("-1", -1), ("5000", -1), ("12x", -1), ("auto", -1)])
 def test_threshold_environment(env, expect):
     code = ("from score_function_top_amd import router;"
             "print(router.get_topk_path_threshold())")

@@ -23,7 +23,7 @@ def _gpu():
         pytest.skip("no GPU")
     router.load()
     yield
-    router.set_topk_path_threshold(8)
+    router.set_topk_path_threshold(router.TOPK_PATH_AUTO)
 
 
 def wl_variant(base, **kw):
@@ -237,6 +237,26 @@ def test_random_configs(T, E, K, sf, renorm, b, G, Kg, dtype, seed):
     assert_close(f64(dx), ref, dtype, f"{wl.name} grad", extra=ext)
 
 
+@pytest.mark.parametrize("E,K,sf,b,dtype", [
+    (4090, 6, synth.SIGMOID, 0.05, synth.F32), (4090, 8, synth.SIGMOID, 0.05, synth.F32),
+    (4094, 12, synth.SIGMOID, 0.0, synth.F32), (4090, 6, synth.SIGMOID, 0.05, synth.BF16),
+    (4090, 6, synth.SOFTMAX, 0.0, synth.F32), (2302, 6, synth.SIGMOID, 0.05, synth.F32)])
+def test_elementwise_padding_lanes(E, K, sf, b, dtype):
+    """Element-wise rows (E not a multiple of 4) whose last chunk is padding
+    on some lanes only, with the LDS group stage and the pruned select: the
+    intermediate, probs and map of every lane match the oracle.  (A
+    lane-divergent branch around the padding test once let the lanes with
+    padding store another element's raw logit as the intermediate.)"""
+    for thr in (router.TOPK_PATH_AUTO, 0, 4096):
+        router.set_topk_path_threshold(thr)
+        try:
+            run_fwd(edge_wl(3, E, K, sf, True, bias=b, G=2, Kg=2, dtype=dtype, c=1.25,
+                            seed=646769))
+            run_fwd(edge_wl(67, E, K, sf, False, bias=b, dtype=dtype, seed=5))
+        finally:
+            router.set_topk_path_threshold(router.TOPK_PATH_AUTO)
+
+
 def test_grouped_softmax():
     run_fwd(edge_wl(300, 256, 8, synth.SOFTMAX, True, G=8, Kg=4, seed=13))
 
@@ -370,7 +390,11 @@ def test_ties(E, K):
 
 PATH_CASES = [(512, 2304, 36, synth.SOFTMAX, 0.0, 0), (700, 256, 4, synth.SOFTMAX, 0.0, 0),
               (700, 512, 22, synth.SIGMOID, 0.1, 0), (300, 256, 8, synth.SIGMOID, 0.05, 8),
-              (300, 100, 30, synth.SOFTMAX, 0.0, 0), (90, 2304, 8, synth.SIGMOID, 0.0, 0)]
+              (300, 100, 30, synth.SOFTMAX, 0.0, 0), (90, 2304, 8, synth.SIGMOID, 0.0, 0),
+              # around the automatic crossovers (4, 8 and 16+ elements per lane)
+              (333, 64, 5, synth.SOFTMAX, 0.0, 0), (333, 64, 4, synth.SIGMOID, 0.0, 0),
+              (257, 128, 4, synth.SOFTMAX, 0.0, 0), (257, 512, 2, synth.SIGMOID, 0.1, 0),
+              (129, 2304, 3, synth.SOFTMAX, 0.0, 0), (129, 1000, 2, synth.SOFTMAX, 0.0, 0)]
 
 
 @pytest.mark.parametrize("T,E,K,sf,b,G", PATH_CASES)
@@ -379,12 +403,12 @@ def test_path_parity(T, E, K, sf, b, G):
     wl = edge_wl(T, E, K, sf, True, bias=b, G=G, Kg=4 if G else 0, c=2.0, seed=23)
     outs = []
     try:
-        for thr in (0, 8, 4096):
+        for thr in (router.TOPK_PATH_AUTO, 0, 8, 4096):
             router.set_topk_path_threshold(thr)
-            r = run_fwd(wl, check=(thr == 8))
+            r = run_fwd(wl, check=(thr == router.TOPK_PATH_AUTO))
             outs.append((f64(r["probs"]), f64(r["map"]), f64(r["inter"])))
     finally:
-        router.set_topk_path_threshold(8)
+        router.set_topk_path_threshold(router.TOPK_PATH_AUTO)
     # maps are identical; weights may differ in the last bits where the
     # paths use different lane-group widths (different reduction trees)
     for o in outs[1:]:

@@ -263,13 +263,16 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
         thr = auto_threshold(4 * a.nch);
     }
     int sel = K < thr ? SEL_ARGMAX : SEL_PRUNE;
+    // the pruned sort takes K <= 2 * lanes where prune_top2 holds (no
+    // groups, fewer than 64 lanes), else K <= lanes
     if (sel == SEL_PRUNE)
-        c.lpt = widen(c.lpt, K);
+        c.lpt = widen(c.lpt, G > 0 ? K : (K + 1) / 2);
     if (G > 0)
         c.lpt = widen(c.lpt, G);
     if (!fill_nch(c, E))
         return ROUTER_ERR_UNSUPPORTED;
-    if (sel == SEL_PRUNE && K > c.lpt)
+    if (sel == SEL_PRUNE && K > (prune_top2(c.lpt, G > 0 ? GROUP_LDS : GROUP_NONE) ? 2 * c.lpt
+                                                                                  : c.lpt))
         sel = SEL_BITS;
 
     const bool reg = g_group_stage.load() == ROUTER_GROUP_STAGE_AUTO && G > 0 &&

@@ -316,6 +316,20 @@ __device__ __forceinline__ void sort_desc64x2(uint64_t &v0, uint64_t &v1)
     v1 = cleaners64<LPT / 2>(n1);
 }
 
+// The same for 32-bit values.
+template <int LPT>
+__device__ __forceinline__ void sort_desc32x2(uint32_t &v0, uint32_t &v1)
+{
+    v0 = sort_desc32<LPT>(v0);
+    v1 = sort_desc32<LPT>(v1);
+    const uint32_t p0 = shfl_mirror<LPT>(v1);
+    const uint32_t p1 = shfl_mirror<LPT>(v0);
+    const uint32_t n0 = v0 > p0 ? v0 : p0;
+    const uint32_t n1 = v1 > p1 ? p1 : v1;
+    v0 = cleaners32<LPT / 2>(n0);
+    v1 = cleaners32<LPT / 2>(n1);
+}
+
 // ------------------------------------------------------------ keys, bf16
 
 // Monotone map of a finite float to an unsigned key: a < b  <=>  key(a) <

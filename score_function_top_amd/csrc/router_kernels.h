@@ -262,25 +262,46 @@ __device__ __forceinline__ Thresh select_bits(const float (&key)[NCH][4], int K,
     return Thresh{v, J};
 }
 
-// prune: keys >= tau (the K-th largest lane maximum; K lanes hold a key >=
-// tau, so the K-th largest key is >= tau) are compacted into this group's
-// LDS list -- raw key bits and ~j, 2*LPT slots plus one dummy slot per lane
-// for the writes of non-candidates -- read back at most two per lane,
-// packed, bitonic-sorted, and the K-th taken.  When the (K+1)-th has a
-// different key, no tie straddles the threshold and j_t is "all".  Falls back
-// to select_bits for the whole wave when a group has more than 2*LPT
-// candidates.  Requires K <= LPT.
-template <int LPT, int NCH>
+// prune: keys >= tau are compacted into this group's LDS list -- raw key
+// bits and ~j, 2*LPT slots plus one dummy slot per lane for the writes of
+// non-candidates -- read back at most two per lane, packed, bitonic-sorted,
+// and the K-th taken.  tau is the K-th largest lane maximum for K <= LPT
+// (K lanes hold a key >= tau, so the K-th largest key is >= tau), and for
+// LPT < K <= 2*LPT the K-th largest of the lanes' two largest keys (2*LPT
+// distinct elements, K of them >= tau: the same bound).  When the (K+1)-th
+// candidate has a different key, no tie straddles the threshold and j_t is
+// "all".  Falls back to select_bits for the whole wave when a group has
+// more than 2*LPT candidates.  Requires K <= LPT, or K <= 2*LPT with TOP2.
+// The two-key bound is compiled only into the kernels without groups and
+// with 16 or 32 lanes per token: in the group-limited kernels (capped at
+// few registers) it cost spills, and 64-lane tokens take K <= 64 anyway.
+template <int LPT, int NCH, bool TOP2>
 __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K, int lane,
                                                int j_lane, uint64_t *cand)
 {
-    float lm = -INFINITY;
+    float tau;
+    if (!TOP2 || K <= LPT) {
+        float lm = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < NCH; c++)
+        for (int c = 0; c < NCH; c++)
 #pragma unroll
-        for (int u = 0; u < 4; u++)
-            lm = fmaxf(lm, key[c][u]);
-    float tau = ord_key_inv(group_bcast<LPT>(sort_desc32<LPT>(ord_key(lm + 0.0f)), K - 1));
+            for (int u = 0; u < 4; u++)
+                lm = fmaxf(lm, key[c][u]);
+        tau = ord_key_inv(group_bcast<LPT>(sort_desc32<LPT>(ord_key(lm + 0.0f)), K - 1));
+    } else {
+        // the lane's two largest keys (two elements; equal values allowed)
+        float m1 = -INFINITY, m2 = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                m2 = fmaxf(m2, fminf(m1, key[c][u]));
+                m1 = fmaxf(m1, key[c][u]);
+            }
+        uint32_t a = ord_key(m1 + 0.0f), b = ord_key(m2 + 0.0f);
+        sort_desc32x2<LPT>(a, b);
+        tau = ord_key_inv(group_bcast<LPT>(b, K - 1 - LPT));  // position K-1 >= LPT
+    }
     tau = fmaxf(tau, kMinKey);  // padding and excluded experts never compete
     uint32_t cnt = 0;
 #pragma unroll
@@ -312,18 +333,29 @@ __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K
     };
     uint64_t v0 = cand[lane];
     v0 = (uint32_t)lane < total ? repack(v0) : 0ull;
-    uint64_t next;
+    uint64_t next, t64 = 0;
     if (wave_any(total > (uint32_t)LPT)) {
         uint64_t v1 = cand[lane + LPT];
         v1 = (uint32_t)(lane + LPT) < total ? repack(v1) : 0ull;
         sort_desc64x2<LPT>(v0, v1);
-        // the (K+1)-th: position K, in the second half when K == LPT
-        next = K < LPT ? group_bcast64<LPT>(v0, K) : group_bcast64<LPT>(v1, 0);
+        // the K-th and (K+1)-th are positions K-1 and K of the 2*LPT slots
+        if constexpr (TOP2) {
+            if (K > LPT)
+                t64 = group_bcast64<LPT>(v1, K - 1 - LPT);
+            next = K < LPT ? group_bcast64<LPT>(v0, K)
+                           : (K < 2 * LPT ? group_bcast64<LPT>(v1, K - LPT) : 0ull);
+        } else {
+            next = K < LPT ? group_bcast64<LPT>(v0, K) : group_bcast64<LPT>(v1, 0);
+        }
     } else {
+        // no group of the wave has more than LPT candidates: every token of
+        // the wave has K <= LPT (with K > LPT the wave is idle, past T, and
+        // stores nothing)
         v0 = sort_desc64<LPT>(v0);
         next = K < LPT ? group_bcast64<LPT>(v0, K) : 0ull;
     }
-    const uint64_t t64 = group_bcast64<LPT>(v0, K - 1);  // K <= LPT: in the first half
+    if (!TOP2 || K <= LPT)
+        t64 = group_bcast64<LPT>(v0, K - 1);  // in the first half
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     Thresh t = unpack_thresh(t64);
@@ -756,7 +788,8 @@ fwd_kernel(FwdParams p)
         } else {
             const Thresh t = p.sel == SEL_BITS
                                  ? select_bits<LPT, NCH>(key, p.K, j_lane)
-                                 : select_prune<LPT, NCH>(key, p.K, lane, j_lane, cand);
+                                 : select_prune<LPT, NCH, prune_top2(LPT, GM)>(key, p.K, lane,
+                                                                               j_lane, cand);
             // idle groups (past T) store nothing; give them a threshold no key meets
             const float tx = tok ? t.x : INFINITY;
             if (!wave_any(t.j != 0xFFFFFFFFu)) {

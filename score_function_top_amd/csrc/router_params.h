@@ -23,6 +23,11 @@ enum { GROUP_NONE = 0, GROUP_LDS = 1, GROUP_REG = 2 };
 // (chunks times groups per chunk) it holds per token: 16 up to two chunks,
 // 8 from three on (16 slots there push the prune kernels past 128 VGPRs).
 constexpr int kGroupRegMaxNch = 4;
+
+// Whether the pruned selection of a forward kernel takes LPT < K <= 2*LPT
+// (the bound from each lane's two largest keys): without groups and with
+// fewer than 64 lanes per token.  The host picks the layout accordingly.
+constexpr bool prune_top2(int lpt, int gm) { return gm == GROUP_NONE && lpt < 64; }
 constexpr int group_reg_slots(int nch) { return nch >= 3 ? 8 : 16; }
 // Built (lanes per token LPT, chunks NCH, log2 of lanes per group LG):
 // L = 2^LG <= LPT and NCH * LPT / L <= group_reg_slots(NCH).

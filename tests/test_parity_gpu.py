@@ -394,7 +394,11 @@ PATH_CASES = [(512, 2304, 36, synth.SOFTMAX, 0.0, 0), (700, 256, 4, synth.SOFTMA
               # around the automatic crossovers (4, 8 and 16+ elements per lane)
               (333, 64, 5, synth.SOFTMAX, 0.0, 0), (333, 64, 4, synth.SIGMOID, 0.0, 0),
               (257, 128, 4, synth.SOFTMAX, 0.0, 0), (257, 512, 2, synth.SIGMOID, 0.1, 0),
-              (129, 2304, 3, synth.SOFTMAX, 0.0, 0), (129, 1000, 2, synth.SOFTMAX, 0.0, 0)]
+              (129, 2304, 3, synth.SOFTMAX, 0.0, 0), (129, 1000, 2, synth.SOFTMAX, 0.0, 0),
+              # lanes < K <= 2 * lanes: the bound from the lanes' two largest keys
+              (300, 256, 36, synth.SOFTMAX, 0.0, 0), (129, 512, 36, synth.SIGMOID, 0.1, 0),
+              (65, 64, 30, synth.SOFTMAX, 0.0, 0), (33, 128, 64, synth.SIGMOID, 0.0, 0),
+              (300, 256, 36, synth.SIGMOID, 0.05, 8), (77, 2304, 100, synth.SOFTMAX, 0.0, 0)]
 
 
 @pytest.mark.parametrize("T,E,K,sf,b,G", PATH_CASES)

@@ -265,10 +265,11 @@ __device__ __forceinline__ Thresh select_bits(const float (&key)[NCH][4], int K,
 // prune: keys >= tau are compacted into this group's LDS list -- raw key
 // bits and ~j, 2*LPT slots plus one dummy slot per lane for the writes of
 // non-candidates -- read back at most two per lane, packed, bitonic-sorted,
-// and the K-th taken.  tau is the K-th largest lane maximum for K <= LPT
-// (K lanes hold a key >= tau, so the K-th largest key is >= tau), and for
-// LPT < K <= 2*LPT the K-th largest of the lanes' two largest keys (2*LPT
-// distinct elements, K of them >= tau: the same bound).  When the (K+1)-th
+// and the K-th taken.  tau is the K-th largest lane maximum (K lanes hold
+// a key >= tau, so the K-th largest key is >= tau), or, with TOP2 and
+// 2*K > LPT, the K-th largest of the lanes' two largest keys (2*LPT
+// distinct elements, K of them >= tau: the same bound, tighter when K is a
+// large share of the lanes, and valid up to K = 2*LPT).  When the (K+1)-th
 // candidate has a different key, no tie straddles the threshold and j_t is
 // "all".  Falls back to select_bits for the whole wave when a group has
 // more than 2*LPT candidates.  Requires K <= LPT, or K <= 2*LPT with TOP2.
@@ -280,7 +281,7 @@ __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K
                                                int j_lane, uint64_t *cand)
 {
     float tau;
-    if (!TOP2 || K <= LPT) {
+    if (!TOP2 || 2 * K <= LPT) {
         float lm = -INFINITY;
 #pragma unroll
         for (int c = 0; c < NCH; c++)
@@ -300,7 +301,8 @@ __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K
             }
         uint32_t a = ord_key(m1 + 0.0f), b = ord_key(m2 + 0.0f);
         sort_desc32x2<LPT>(a, b);
-        tau = ord_key_inv(group_bcast<LPT>(b, K - 1 - LPT));  // position K-1 >= LPT
+        tau = ord_key_inv(K <= LPT ? group_bcast<LPT>(a, K - 1)
+                                   : group_bcast<LPT>(b, K - 1 - LPT));
     }
     tau = fmaxf(tau, kMinKey);  // padding and excluded experts never compete
     uint32_t cnt = 0;

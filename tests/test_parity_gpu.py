@@ -398,7 +398,8 @@ PATH_CASES = [(512, 2304, 36, synth.SOFTMAX, 0.0, 0), (700, 256, 4, synth.SOFTMA
               # lanes < K <= 2 * lanes: the bound from the lanes' two largest keys
               (300, 256, 36, synth.SOFTMAX, 0.0, 0), (129, 512, 36, synth.SIGMOID, 0.1, 0),
               (65, 64, 30, synth.SOFTMAX, 0.0, 0), (33, 128, 64, synth.SIGMOID, 0.0, 0),
-              (300, 256, 36, synth.SIGMOID, 0.05, 8), (77, 2304, 100, synth.SOFTMAX, 0.0, 0)]
+              (300, 256, 36, synth.SIGMOID, 0.05, 8), (77, 2304, 100, synth.SOFTMAX, 0.0, 0),
+              (300, 128, 12, synth.SOFTMAX, 0.0, 0), (129, 64, 9, synth.SIGMOID, 0.1, 0)]
 
 
 @pytest.mark.parametrize("T,E,K,sf,b,G", PATH_CASES)

@@ -262,6 +262,32 @@ def test_elementwise_padding_lanes(E, K, sf, b, dtype):
             router.set_topk_path_threshold(router.TOPK_PATH_AUTO)
 
 
+def _random_aux_cases(n=24, seed=2026):
+    """Aux-score shapes drawn like _random_cases (no bias or groups: the aux
+    map is the plain top-K of the logits)."""
+    return [(T, E, K, sf, renorm, dtype, sd)
+            for T, E, K, sf, renorm, _b, _G, _Kg, dtype, sd in _random_cases(n, seed)]
+
+
+@pytest.mark.parametrize("T,E,K,sf,renorm,dtype,seed", _random_aux_cases())
+def test_random_aux(T, E, K, sf, renorm, dtype, seed):
+    """Aux scores forward (map exact, scores and intermediate within
+    tolerance) and backward, isolated and chained, on seeded random shapes."""
+    wl = dataclasses.replace(edge_wl(T, E, K, sf, dtype=dtype, seed=seed), aux_renorm=renorm)
+    r = run_aux_fwd(wl)
+    g_st, g64 = grads(wl, T, aux=True)
+    s32 = r["S"].astype(np.float32)
+    dx = router.router_aux_scores_bwd(to_dev(g_st, dtype), torch.from_numpy(s32).to(DEV),
+                                      SCORE_NAME[sf], renorm)
+    dxc = router.router_aux_scores_bwd(to_dev(g_st, dtype), r["inter"], SCORE_NAME[sf], renorm)
+    torch.cuda.synchronize()
+    ref = oracle.aux_bwd(g64, s32.astype(np.float64), sf, renorm, threads=threads())
+    assert_close(f64(dx), ref, dtype, f"{wl.name} aux grad")
+    refc = oracle.aux_bwd(g64, r["S"], sf, renorm, threads=threads())
+    ext = chain_tol(g64, r["S"], None, K, sf, renorm, 1.0, aux=True)
+    assert_close(f64(dxc), refc, dtype, f"{wl.name} aux chained grad", extra=ext)
+
+
 def test_grouped_softmax():
     run_fwd(edge_wl(300, 256, 8, synth.SOFTMAX, True, G=8, Kg=4, seed=13))
 

@@ -352,9 +352,20 @@ __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K
     } else {
         // no group of the wave has more than LPT candidates: every token of
         // the wave has K <= LPT (with K > LPT the wave is idle, past T, and
-        // stores nothing)
-        v0 = sort_desc64<LPT>(v0);
-        next = K < LPT ? group_bcast64<LPT>(v0, K) : 0ull;
+        // stores nothing).  32-lane groups with at most 16 candidates
+        // everywhere sort only their first 16 lanes (the others hold no
+        // candidate): positions K-1 and K are then in those lanes, or K is
+        // 16 and equals the count, so there is no (K+1)-th.  (Compiled into
+        // the 64-lane kernels the same branch slowed the 2304-expert forward
+        // by 3%, where it is never taken.)
+        constexpr int H = LPT == 32 ? 16 : LPT;
+        if (H < LPT && !wave_any(total > (uint32_t)H)) {
+            v0 = sort_desc64<H>(v0);
+            next = K < H ? group_bcast64<LPT>(v0, K) : 0ull;
+        } else {
+            v0 = sort_desc64<LPT>(v0);
+            next = K < LPT ? group_bcast64<LPT>(v0, K) : 0ull;
+        }
     }
     if (!TOP2 || K <= LPT)
         t64 = group_bcast64<LPT>(v0, K - 1);  // in the first half

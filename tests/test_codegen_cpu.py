@@ -44,19 +44,19 @@ def join_block_writes(asm):
         m = re.match(r"^(\.LBB\w+):", line)
         if not m or m.group(1) not in targets:
             continue
-        pre = []
-        for t in (x.strip() for x in lines[i + 1:i + 40]):
+        pre, restored = [], False
+        for t in (x.strip() for x in lines[i + 1:i + 400]):
             if not t or t.startswith(";"):
                 continue
             if re.match(r"s_or_b64 exec, exec, ", t):
+                restored = True
                 break
-            if t.startswith((".LBB", "s_cbranch", "s_branch")) or "saveexec" in t:
-                pre = []  # no restore of this branch here
-                break
+            if t.startswith((".LBB", "s_cbranch", "s_branch", "s_endpgm")) or "saveexec" in t:
+                break  # the block ends without restoring this branch's mask
             pre.append(t)
         vec = [p for p in pre if p.startswith("v_")
                and not re.match(r"v_(readlane|readfirstlane|writelane)", p)]
-        if vec:
+        if restored and vec:
             found.append((owner[m.group(1)], m.group(1), vec))
     return found
 
@@ -70,6 +70,9 @@ def test_detector_flags_a_write_ahead_of_the_restore():
     ok = asm.replace("\tv_mov_b32_e32 v174, v144\n\ts_or_b64 exec, exec, s[4:5]",
                      "\ts_or_b64 exec, exec, s[4:5]\n\tv_mov_b32_e32 v174, v144")
     assert join_block_writes(ok) == []
+    # a skip target whose block never restores a mask is not this pattern
+    skip = asm.replace("\ts_or_b64 exec, exec, s[4:5]\n", "")
+    assert join_block_writes(skip) == []
 
 
 def _asm(src, out_dir):

@@ -375,12 +375,21 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b)
     return as_f((uint32_t)b << 16);
 }
 
-// Round to nearest even; finite inputs.
+// Two fp32 values to a packed pair of bf16 (low half from `lo`), rounded
+// to nearest even by the gfx950 packed conversion (v_cvt_pk_bf16_f32: one
+// instruction for two values, against four integer operations each for
+// the rounding done by hand).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = as_u(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return (uint16_t)f32x2_to_bf16x2(f, 0.0f);
 }
 
 }  // namespace rdev

@@ -77,8 +77,8 @@ template <> struct io<uint16_t> {
     __device__ static void store4(rsrc_t r, uint32_t off, const float (&v)[4])
     {
         __attribute__((ext_vector_type(2))) uint32_t t;
-        t[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        t[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        t[0] = f32x2_to_bf16x2(v[0], v[1]);
+        t[1] = f32x2_to_bf16x2(v[2], v[3]);
         __builtin_amdgcn_raw_buffer_store_b64(t, r, (int)off, 0, kStream);
     }
     __device__ static void store1(rsrc_t r, uint32_t off, float v)

@@ -308,6 +308,9 @@ GROUP_STAGE_CASES = [
     (65, 768, 12, 6, 3, synth.BF16, synth.SOFTMAX, 0.0),    # three chunks
     (100, 64, 8, 16, 8, synth.F32, synth.SIGMOID, 0.05),    # 1 lane per group, 16 slots, q = 1
     (80, 1024, 4, 4, 2, synth.BF16, synth.SOFTMAX, 0.0),    # 64 lanes per group
+    # bias with q = 3 and 4 in two-chunk kernels: the group stage's pruning bound
+    (300, 256, 16, 8, 4, synth.BF16, synth.SIGMOID, 0.05),  # 32 lanes, q = 4
+    (150, 128, 12, 4, 4, synth.F32, synth.SIGMOID, 0.05),   # 16 lanes, q = 3
 ]
 
 

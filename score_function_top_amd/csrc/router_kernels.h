@@ -276,7 +276,7 @@ __device__ __forceinline__ Thresh select_bits(const float (&key)[NCH][4], int K,
 // The two-key bound is compiled only into the kernels without groups and
 // with 16 or 32 lanes per token: in the group-limited kernels (capped at
 // few registers) it cost spills, and 64-lane tokens take K <= 64 anyway.
-template <int LPT, int NCH, bool TOP2>
+template <int LPT, int NCH, bool TOP2, bool KEYS32>
 __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K, int lane,
                                                int j_lane, uint64_t *cand, bool use_bound,
                                                float bound)
@@ -333,6 +333,46 @@ __device__ __forceinline__ Thresh select_prune(const float (&key)[NCH][4], int K
         }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    // Keys alone first: sort the candidates' 32-bit order keys (half the
+    // work of the 64-bit words).  When no group of the wave has equal keys
+    // at positions K-1 and K, the K-th key alone is the threshold: exactly
+    // the K keys at or above it are selected.  Only such a tie needs the
+    // indices, i.e. the 64-bit sort further down (the list is still there).
+    // Compiled into the 16- and 32-lane kernels without the register group
+    // stage only: the register-capped group-limited kernels spilled with it,
+    // and the 64-lane forward of 2304 experts ran 2% slower with it (a
+    // memory-bound kernel; its candidate sort is not what limits it).
+    if constexpr (KEYS32) {
+        const uint32_t *ck = reinterpret_cast<const uint32_t *>(cand);
+        auto okey = [&](int i) { return ord_key(as_f(ck[2 * i + 1]) + 0.0f); };  // key bits
+        uint32_t a0 = (uint32_t)lane < total ? okey(lane) : 0u;
+        uint32_t xk, xn;
+        if (wave_any(total > (uint32_t)LPT)) {
+            uint32_t a1 = (uint32_t)(lane + LPT) < total ? okey(lane + LPT) : 0u;
+            sort_desc32x2<LPT>(a0, a1);
+            xk = K <= LPT ? group_bcast<LPT>(a0, K - 1)
+                          : group_bcast<LPT>(a1, (K - 1 - LPT) & (LPT - 1));
+            xn = K < LPT ? group_bcast<LPT>(a0, K)
+                         : (K < 2 * LPT ? group_bcast<LPT>(a1, K - LPT) : 0u);
+        } else {
+            constexpr int H = LPT == 32 ? 16 : LPT;  // as for the 64-bit sort below
+            if (H < LPT && !wave_any(total > (uint32_t)H)) {
+                a0 = sort_desc32<H>(a0);
+                xn = K < H ? group_bcast<LPT>(a0, K) : 0u;
+            } else {
+                a0 = sort_desc32<LPT>(a0);
+                xn = K < LPT ? group_bcast<LPT>(a0, K) : 0u;
+            }
+            xk = group_bcast<LPT>(a0, K <= LPT ? K - 1 : LPT - 1);
+        }
+        // candidates' keys are never 0 (finite floats map above it); idle
+        // groups have none, so xn == 0 there
+        if (!wave_any(xn != 0u && xn == xk)) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            return Thresh{ord_key_inv(xk), 0xFFFFFFFFu};
+        }
+    }
     auto repack = [](uint64_t raw) {
         return ((uint64_t)ord_key(as_f((uint32_t)(raw >> 32)) + 0.0f) << 32) | (uint32_t)raw;
     };
@@ -837,7 +877,7 @@ fwd_kernel(FwdParams p)
         } else {
             const Thresh t = p.sel == SEL_BITS
                                  ? select_bits<LPT, NCH>(key, p.K, j_lane)
-                                 : select_prune<LPT, NCH, prune_top2(LPT, GM)>(
+                                 : select_prune<LPT, NCH, prune_top2(LPT, GM), GM != GROUP_REG && LPT < 64>(
                                        key, p.K, lane, j_lane, cand,
                                        // the bound's live values spilled the
                                        // register-capped 4-chunk kernels

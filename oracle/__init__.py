@@ -50,6 +50,7 @@ def _load(path=None):
                                     ctypes.c_double, d, d, u8, d, d]
     lib.oracle_topk_bwd.argtypes = [d, d, u8, i64, i32, i32, i32, i32,
                                     ctypes.c_double, d]
+    lib.oracle_select.argtypes = [d, d, i64, i32, i32, i32, i32, u8, d]
     lib.oracle_aux_fwd.argtypes = [d, i64, i32, i32, i32, i32, d, u8, d]
     lib.oracle_aux_bwd.argtypes = [d, d, i64, i32, i32, i32, d]
     q = ctypes.POINTER(ctypes.c_int64)
@@ -61,7 +62,7 @@ def _load(path=None):
     lib.oracle_route_maps.argtypes = [d, i32, i32, i32, i32, i32, d, i32p, i32p, i32p, i32p, q]
     lib.oracle_topk_shared_gate.argtypes = [d, d, d, i64, i32, i32, i32, i32, i32,
                                             ctypes.c_double, i32, i64, d, i32p]
-    for f in (lib.oracle_topk_fwd, lib.oracle_topk_bwd, lib.oracle_aux_fwd,
+    for f in (lib.oracle_topk_fwd, lib.oracle_topk_bwd, lib.oracle_select, lib.oracle_aux_fwd,
               lib.oracle_aux_bwd, lib.oracle_tokens_per_expert, lib.oracle_aux_loss,
               lib.oracle_aux_loss_bwd, lib.oracle_route_maps, lib.oracle_topk_shared_gate):
         f.restype = ctypes.c_int
@@ -129,6 +130,38 @@ def topk_fwd(x, K, score_fn=SOFTMAX, renorm=False, num_groups=0,
     if err:
         raise OracleError("oracle_topk_fwd rejected its arguments")
     return probs, rmap, inter, margin
+
+
+def select(key, K, num_groups=0, group_topk=0, gval=None, threads=1, lib=None):
+    """The forward's selection step on given keys: returns (routing_map
+    [T,E] u8, margin [T] f64) for expert-stage keys ``key`` [T,E] and, with
+    groups, group values ``gval`` [T,E] (fp32 values; group scores are
+    their fp32 sums)."""
+    lib = lib or _load()
+    key = _f64(key)
+    T, E = key.shape
+    gv = None
+    if num_groups:
+        gv = _f64(gval)
+        if gv.shape != key.shape:
+            raise OracleError("gval must have the shape of key")
+    rmap = np.empty((T, E), np.uint8)
+    margin = np.empty((T,), np.float64)
+    err = []
+
+    def fn(t0, t1):
+        r = lib.oracle_select(
+            _p(key[t0:t1], ctypes.c_double),
+            None if gv is None else _p(gv[t0:t1], ctypes.c_double), t1 - t0, E, K,
+            num_groups, group_topk, _p(rmap[t0:t1], ctypes.c_uint8),
+            _p(margin[t0:t1], ctypes.c_double))
+        if r != 0:
+            err.append(r)
+
+    _run(T, threads, fn)
+    if err:
+        raise OracleError("oracle_select rejected its arguments")
+    return rmap, margin
 
 
 def topk_bwd(g, s, m, K, score_fn=SOFTMAX, renorm=False, scaling_factor=1.0,

@@ -236,6 +236,41 @@ int oracle_topk_fwd(const double *x, int64_t T, int E, int K, int score_fn,
     return 0;
 }
 
+/*
+ * The selection step alone, for keys and group values given per token:
+ *   key [T,E]    expert-stage selection keys
+ *   gval [T,E]   group values (fp32 values promoted to fp64); read only
+ *                when G > 0
+ *   map [T,E]    1 on the selected experts, else 0
+ *   margin [T]   optional, as in select_row
+ * The same rule as the forward (group score = fp32 sum of the q = K/Kg
+ * largest group values, largest first; Kg best groups, ties to the lower
+ * group; then the K largest keys among their experts, ties to the lower
+ * expert).  Lets a caller decide a selection from keys computed elsewhere,
+ * e.g. from another implementation's fp32 scores.
+ * Returns 0, or -1 for arguments outside the operation's domain.
+ */
+int oracle_select(const double *key, const double *gval, int64_t T, int E,
+                  int K, int G, int Kg, uint8_t *map, double *margin)
+{
+    int64_t t;
+    keyed *work;
+
+    if (T < 0 || E < 1 || K < 1 || K > E || E > 1 << 20)
+        return -1;
+    if (G > 0 && (E % G != 0 || Kg < 1 || Kg > G || K % Kg != 0 ||
+                  K / Kg > E / G || G > 4096 || !gval))
+        return -1;
+    work = (keyed *)malloc(sizeof(keyed) * (size_t)E);
+    if (!work)
+        return -1;
+    for (t = 0; t < T; t++)
+        select_row(key + t * E, G > 0 ? gval + t * E : NULL, E, K, G, Kg,
+                   map + t * E, work, margin ? margin + t : NULL);
+    free(work);
+    return 0;
+}
+
 /* ------------------------------------------------------------- topk bwd */
 
 /*

@@ -284,6 +284,32 @@ def pin_groups_bruteforce(lib):
     assert (m0 == m1).all() and (m0 == m2).all()
 
 
+def pin_select_bruteforce(lib):
+    """The selection step on given keys and group values equals brute force
+    over every subset of groups and of experts (tiny tie-heavy rows, keys
+    independent of the group values), and, fed the forward's own keys, it
+    reproduces the forward's map and margin."""
+    rng = np.random.default_rng(17)
+    for (E, G, Kg, K) in ((6, 0, 0, 1), (9, 0, 0, 3), (8, 4, 2, 4), (12, 6, 3, 3),
+                          (12, 4, 2, 2), (6, 3, 1, 2), (12, 6, 2, 4)):
+        key = rng.integers(-2, 3, (5, E)).astype(np.float64)
+        gv = (rng.integers(0, 4, (5, E)) * 0.25).astype(np.float32).astype(np.float64)
+        m, _ = oracle.select(key, K, G, Kg, gv if G else None, lib=lib)
+        for t in range(5):
+            allowed = None
+            if G:
+                kept = brute_group_select(gv[t], G, Kg, K // Kg)
+                allowed = np.repeat(kept, E // G)
+            assert (m[t] == brute_select(key[t], K, allowed)).all(), (E, G, Kg, K, t)
+    x = rng.normal(0, 1, (7, 24))
+    b = rng.uniform(-0.1, 0.1, 24).astype(np.float32).astype(np.float64)
+    _, m0, _, mg0 = oracle.topk_fwd(x, 6, oracle.SIGMOID, True, 4, 2, 1.0, b, lib=lib)
+    gv = np.stack([group_values(r, oracle.SIGMOID, b) for r in x]).astype(np.float64)
+    m1, mg1 = oracle.select(gv, 6, 4, 2, gv, lib=lib)
+    assert (m0 == m1).all()
+    close(mg1, mg0, rtol=0, atol=0, what="select margin")
+
+
 def pin_renorm_identities(lib):
     """Renormalised probs sum to c; softmax renorm is scipy's softmax over
     the selected logits; with K = E the topk scores equal the aux scores."""
@@ -614,7 +640,7 @@ def pin_shared_gate_invariants(lib):
 
 
 PINS = [pin_golden, pin_score_library, pin_topk_bruteforce,
-        pin_groups_bruteforce, pin_renorm_identities, pin_scale_linearity,
+        pin_groups_bruteforce, pin_select_bruteforce, pin_renorm_identities, pin_scale_linearity,
         pin_backward_fd, pin_aux_backward_fd, pin_backward_invariants,
         pin_rows_independent, pin_margin, pin_tokens_per_expert,
         pin_aux_loss_closed_forms, pin_aux_loss_fd, pin_route_maps_bruteforce,

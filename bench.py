@@ -578,8 +578,10 @@ def main():
 
     sets = [new_set() for _ in range(n_sets)]
     ws_bytes = router.router_aux_loss_workspace_bytes(T, E)
+    cws_bytes = router.router_tokens_per_expert_workspace_bytes(T, E)
     for s in sets:
         s["cnt"] = torch.zeros(E, dtype=torch.int64, device=dev)
+        s["cws"] = torch.zeros(cws_bytes, dtype=torch.uint8, device=dev)
         s["loss"] = torch.empty((), dtype=torch.float32, device=dev)
         s["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     grad_loss = torch.ones(1, dtype=torch.float32, device=dev)
@@ -599,7 +601,7 @@ def main():
             router.router_aux_scores_bwd(s["ag"], s["ainter"], sname, wl.aux_renorm,
                                          out=s["adx"])
         elif kind == "tokens_per_expert":
-            router.router_tokens_per_expert(s["amap"], out=s["cnt"])
+            router.router_tokens_per_expert(s["amap"], out=s["cnt"], workspace=s["cws"])
         elif kind == "aux_loss_fwd":
             router.router_aux_loss_fwd(s["ascores"], s["cnt"], T, K, synth.AUX_LOSS_COEFF,
                                        out=s["loss"], workspace=s["ws"])
@@ -772,8 +774,8 @@ def main():
                 torch, [lambda i=i: launch(kind, sets[(i + k0) % n_sets])
                         for i in range(args.steps)])
             sym = KERNEL_SYMBOL[kind]
-            loss[kind] = {"kernels": (["zero_counts_kernel"] if sym == "count_kernel" else [])
-                          + [sym] + (["loss_final_kernel"] if sym == "loss_kernel" else []),
+            loss[kind] = {"kernels": [sym] + (["loss_final_kernel"] if sym == "loss_kernel"
+                                              else []),
                           "us_avg": round(avg, 2), "us_graph": round(g_us, 2),
                           "algo_bytes": nb, "GBps": round(nb / avg / 1e3, 1),
                           "GBps_graph": round(nb / g_us / 1e3, 1),

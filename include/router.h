@@ -30,6 +30,8 @@
  *           router_aux_loss_workspace_bytes(T, E) bytes or more, with any
  *           contents; it is scratch for the duration of the call's kernels
  *           and must not be shared by calls that may run concurrently.
+ *           router_tokens_per_expert takes one that starts zero-filled and
+ *           is left zero-filled (see there).
  * Dtypes.   `dtype` (router_dtype) is the storage type of logits, probs,
  *           scores and gradients.  intermediate is always fp32 and the
  *           routing map is one byte per element holding 0 or 1 (a torch
@@ -184,17 +186,30 @@ router_status router_aux_scores_bwd(const void *grad_scores,
  * least 256); 0 when T or E is out of range. */
 size_t router_aux_loss_workspace_bytes(int64_t T, int32_t E);
 
+/* Bytes of workspace router_tokens_per_expert needs for T rows of E
+ * experts (at least 256; depends on E only, at most 65536 for E <= 4096);
+ * 0 when T or E is out of range. */
+size_t router_tokens_per_expert_workspace_bytes(int64_t T, int32_t E);
+
 /*
  * router_tokens_per_expert -- tokens_per_expert[i] = number of rows t of
  * routing_map [T,E] (uint8) with a nonzero byte at (t, i); int64 [E] out.
- * Exact (integer atomics).  T == 0 writes zeros.  Errors: E < 1 or T < 0
+ * Exact (integer atomics), one kernel launch.  The workspace (device
+ * memory, router_tokens_per_expert_workspace_bytes(T, E) bytes or more,
+ * 8-byte aligned) holds a per-expert accumulator that also counts the
+ * contributions it received: it
+ * must be zero-filled before its first use (e.g. allocated with zeros), and
+ * every call leaves it zero-filled again, so later calls ordered after this
+ * one (same stream) can reuse it; calls that may run concurrently need
+ * separate workspaces.  T == 0 writes zeros.  Errors: E < 1 or T < 0
  * INVALID_ARG, E > ROUTER_MAX_EXPERTS or T > 2^32 - 1 UNSUPPORTED, T*E
- * bytes overflowing OVERFLOW; null pointers or counts not 8-byte aligned
- * INVALID_ARG.
+ * bytes overflowing OVERFLOW; null pointers, counts or workspace not
+ * 8-byte aligned, a workspace smaller than the query INVALID_ARG.
  */
 router_status router_tokens_per_expert(const uint8_t *routing_map,
                                        int64_t T, int32_t E,
                                        int64_t *tokens_per_expert,
+                                       void *workspace, size_t workspace_bytes,
                                        void *hip_stream);
 
 /*

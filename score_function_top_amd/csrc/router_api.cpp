@@ -427,23 +427,35 @@ size_t router_aux_loss_workspace_bytes(int64_t T, int32_t E)
     return aux_ws_bytes(T, E);
 }
 
+size_t router_tokens_per_expert_workspace_bytes(int64_t T, int32_t E)
+{
+    if (check_loss_shape(T, E) != ROUTER_OK)
+        return 0;
+    return count_ws_bytes(E);
+}
+
 router_status router_tokens_per_expert(const uint8_t *routing_map, int64_t T, int32_t E,
-                                       int64_t *tokens_per_expert, void *hip_stream)
+                                       int64_t *tokens_per_expert, void *workspace,
+                                       size_t workspace_bytes, void *hip_stream)
 {
     router_status st = check_loss_shape(T, E);
     if (st != ROUTER_OK)
         return st;
-    if (T > (int64_t)UINT32_MAX)  // per-block counts are 32-bit
+    if (T > (int64_t)UINT32_MAX)  // per-column totals are 32-bit
         return ROUTER_ERR_UNSUPPORTED;
-    if (!tokens_per_expert || (T > 0 && !routing_map))
+    if (!tokens_per_expert || !workspace || (T > 0 && !routing_map))
         return ROUTER_ERR_INVALID_ARG;
-    if (!aligned(tokens_per_expert, 8))
+    if (!aligned(tokens_per_expert, 8) || !aligned(workspace, 8) ||
+        workspace_bytes < count_ws_bytes(E))
         return ROUTER_ERR_INVALID_ARG;
-    const int vec = E % 16 == 0 && aligned(routing_map, 16) ? 16
-                    : E % 4 == 0 && aligned(routing_map, 4)  ? 4
-                                                             : 1;
-    const hipError_t e = launch_count(routing_map, vec, count_geo(T, E), tokens_per_expert,
-                                      (hipStream_t)hip_stream);
+    const ColGeo g = count_geo(T, E);
+    const int cpl = 1 << g.cpl_log2;
+    const int vec = cpl >= 16 && E % 16 == 0 && aligned(routing_map, 16)  ? 16
+                    : cpl >= 8 && E % 8 == 0 && aligned(routing_map, 8) ? 8
+                    : E % 4 == 0 && aligned(routing_map, 4)             ? 4
+                                                                         : 1;
+    const hipError_t e = launch_count(routing_map, vec, g, tokens_per_expert,
+                                      (uint64_t *)workspace, (hipStream_t)hip_stream);
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 

@@ -12,13 +12,16 @@
 // with dL/dscores[t,i] = coeff * E * n_i / (N^2 K).
 //
 // All three are column reductions or broadcasts over [T,E] and bound by
-// HBM.  They share one geometry (ColGeo): a lane owns 4 consecutive columns
-// for every row it visits, so its per-column sums and weights live in
+// HBM.  They share one geometry (ColGeo): a lane owns consecutive columns
+// (4 for the loss, 4 to 16 for the counts) for every row it visits, so its per-column sums and weights live in
 // registers, and a wave reads or writes one contiguous row segment per
 // step.  The fp64 loss is reduced across blocks through a workspace and a
 // second one-block kernel in a fixed order, so it is the same bit for bit
-// on every run; the integer counts use atomic adds, exact in any order.
+// on every run; the integer counts use atomic adds, exact in any order, and
+// the last block of each column stripe writes them out (one launch).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "router_io.h"
 #include "router_params.h"
@@ -28,7 +31,7 @@ namespace rker {
 namespace {
 
 struct LaneCols {
-    int col0;      // first of the lane's 4 columns (may be >= E: idle lane)
+    int col0;      // first of the lane's columns (may be >= E: idle lane)
     int row_lane;  // row of this lane within a wave step
 };
 
@@ -90,27 +93,38 @@ __device__ __forceinline__ uint32_t bytes_nonzero(uint32_t w)
     return w & 0x01010101u;
 }
 
-// The lane's 16 map bytes of one row as 4 little-endian words (0 past E).
-// VW = access width: 16 (one 16-byte load; E % 16 == 0), 4 (four 4-byte
-// loads; E % 4 == 0) or 1 (byte loads, any E).
-template <int VW>
-__device__ __forceinline__ void load_map16(rsrc_t r, uint32_t off, int col0, int E,
-                                           uint32_t (&w)[4])
+// The lane's CPL map bytes of one row as CPL/4 little-endian words (0 past
+// E).  VW = access width: CPL (one load; E % CPL == 0), 8 (E % 8 == 0), 4
+// (E % 4 == 0) or 1 (byte loads, any E); a masked access gets the offset
+// kOOB and reads 0.
+template <int CPL, int VW>
+__device__ __forceinline__ void load_map_row(rsrc_t r, uint32_t off, int col0, int E,
+                                             uint32_t (&w)[CPL / 4])
 {
+    constexpr int NW = CPL / 4;
     if constexpr (VW == 16) {
+        static_assert(CPL == 16, "one 16-byte load per 16 columns");
         const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(col0 < E ? off : kOOB), 0,
                                                              kStream);
 #pragma unroll
         for (int q = 0; q < 4; q++)
             w[q] = t[q];
+    } else if constexpr (VW == 8) {
+#pragma unroll
+        for (int q = 0; q < NW / 2; q++) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b64(
+                r, (int)(col0 + 8 * q < E ? off + 8 * q : kOOB), 0, kStream);
+            w[2 * q] = t[0];
+            w[2 * q + 1] = t[1];
+        }
     } else if constexpr (VW == 4) {
 #pragma unroll
-        for (int q = 0; q < 4; q++)
+        for (int q = 0; q < NW; q++)
             w[q] = __builtin_amdgcn_raw_buffer_load_b32(
                 r, (int)(col0 + 4 * q < E ? off + 4 * q : kOOB), 0, kStream);
     } else {
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < NW; q++) {
             w[q] = 0;
 #pragma unroll
             for (int u = 0; u < 4; u++) {
@@ -123,7 +137,7 @@ __device__ __forceinline__ void load_map16(rsrc_t r, uint32_t off, int col0, int
     }
 }
 
-// counts[i] = 0 (runs before count_kernel on the same stream).
+// counts[i] = 0: the whole pass when there are no rows.
 __global__ __launch_bounds__(kBlock) void zero_counts_kernel(int64_t *counts, int E)
 {
     const int i = (int)(blockIdx.x * kBlock + threadIdx.x);
@@ -132,72 +146,88 @@ __global__ __launch_bounds__(kBlock) void zero_counts_kernel(int64_t *counts, in
 }
 
 constexpr int kCountThreads = kCountWaves * 64;
-constexpr int kCountRegion = 64 << kCountCpl;  // counts one wave holds (16 per lane)
 
-// Adds block b's counts (its splits, the columns of its stripe) to
-// counts[] with 64-bit atomic adds.  Integer addition is associative, so
-// the totals do not depend on the order the blocks finish in.  Each lane
-// owns 16 columns; a split's loads are issued in chunks of CH steps (all
-// of them for 16-byte loads) before any is consumed.  Lanes then store
-// their counts to their wave's LDS region (lane l at 16*l, which is
-// row_lane*width + column-in-stripe), and thread i sums column i over the
-// waves and rows of a wave step, so the atomics of a wave hit consecutive
-// addresses.
-template <int VW>
+// Tokens per expert in one launch.  Block b counts its splits of the rows
+// over the columns of its stripe: each lane owns CPL columns and counts its
+// rows' bytes two per 32-bit word (SWAR, 16-bit fields), the loads of up to
+// 16 rows issued before any is consumed (steps are a power of two: chunks
+// of 16, 4 or 1 rows divide them); lanes store their counts to their
+// wave's LDS region (lane l at CPL*l, which is row_lane*width + column in
+// the stripe) and thread i sums column i over the waves and the rows of a
+// wave step.  Column i's 64-bit word in `ws` then takes one device-scope
+// atomic add of (1 << 32) + sum from every block of the stripe: the high
+// half counts the contributions, the low half the routed tokens.  The add
+// that brings the contributions to gsplit (the stripe's block count) is the
+// column's last, so its thread writes the total to counts[] and clears the
+// word: `ws` is zero again when the kernel ends, with no other ordering
+// between blocks than the atomics on each word (one round trip per block;
+// a ticket per stripe and a last-block pass cost three, 11.9 us against
+// about 7 at T=8192, E=2304).  Integer sums are exact in any order.
+template <int CPL, int VW>
 __global__ __launch_bounds__(kCountThreads) void count_kernel(const uint8_t *map, ColGeo g,
-                                                             int64_t *counts)
+                                                             int64_t *counts, uint64_t *ws)
 {
-    constexpr int CH = VW == 1 ? 4 : kCountSteps;
-    __shared__ uint32_t region[kCountWaves * kCountRegion];
+    constexpr int NW = CPL / 4;
+    constexpr int CH = VW == 1 ? 4 : kCountMaxSteps;  // most rows in flight per chunk
+    constexpr int kRegion = 64 * CPL;                  // counts one wave holds
+    __shared__ uint32_t region[kCountWaves * kRegion];
     const int stripe = (int)(blockIdx.x % (unsigned)g.nstripe);
     const int s0 = (int)(blockIdx.x / (unsigned)g.nstripe);
     const int w = wave_index();
     const LaneCols lc = lane_cols(g, stripe);
 
-    uint32_t c[16];
+    uint32_t c[CPL];
 #pragma unroll
-    for (int u = 0; u < 16; u++)
+    for (int u = 0; u < CPL; u++)
         c[u] = 0;
     for (int64_t sp = s0; sp < g.nsplit; sp += g.gsplit) {
         const rsrc_t r = split_rsrc(map, g, sp, 1);
         // bytes b0 and b2 of each word in `lo`, b1 and b3 in `hi`, one
-        // 16-bit field each: at most kCountSteps per field
-        uint32_t lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
-        auto chunk = [&](int k0) {
-            uint32_t v[CH][4];
+        // 16-bit field each: at most kCountMaxSteps per field
+        uint32_t lo[NW], hi[NW];
 #pragma unroll
-            for (int k = 0; k < CH; k++)
-                load_map16<VW>(r,
-                               (uint32_t)split_row(g, w, k0 + k, lc.row_lane) * (uint32_t)g.E +
-                                   (uint32_t)lc.col0,
-                               lc.col0, g.E, v[k]);
+        for (int q = 0; q < NW; q++)
+            lo[q] = hi[q] = 0;
+        // rows of a split in chunks of N (a power of two, at most the steps),
+        // every load of a chunk issued before any is consumed
+        auto rows = [&](auto n) {
+            constexpr int N = decltype(n)::value;
+            for (int k0 = 0; k0 < g.steps; k0 += N) {
+                uint32_t v[N][NW];
 #pragma unroll
-            for (int k = 0; k < CH; k++)
+                for (int k = 0; k < N; k++)
+                    load_map_row<CPL, VW>(
+                        r,
+                        (uint32_t)split_row(g, w, k0 + k, lc.row_lane) * (uint32_t)g.E +
+                            (uint32_t)lc.col0,
+                        lc.col0, g.E, v[k]);
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const uint32_t t = bytes_nonzero(v[k][q]);
-                    lo[q] += t & 0x00010001u;
-                    hi[q] += (t >> 8) & 0x00010001u;
-                }
+                for (int k = 0; k < N; k++)
+#pragma unroll
+                    for (int q = 0; q < NW; q++) {
+                        const uint32_t t = bytes_nonzero(v[k][q]);
+                        lo[q] += t & 0x00010001u;
+                        hi[q] += (t >> 8) & 0x00010001u;
+                    }
+            }
         };
-        if constexpr (CH == kCountSteps) {
-            chunk(0);
-        } else {
-#pragma unroll 1
-            for (int k0 = 0; k0 < kCountSteps; k0 += CH)
-                chunk(k0);
-        }
+        if (g.steps >= CH)
+            rows(std::integral_constant<int, CH>{});
+        else if (g.steps >= 4)
+            rows(std::integral_constant<int, 4>{});
+        else
+            rows(std::integral_constant<int, 1>{});
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < NW; q++) {
             c[4 * q + 0] += lo[q] & 0xFFFFu;
             c[4 * q + 1] += hi[q] & 0xFFFFu;
             c[4 * q + 2] += lo[q] >> 16;
             c[4 * q + 3] += hi[q] >> 16;
         }
     }
-    uint32_t *mine = region + w * kCountRegion + lane_id() * 16;
+    uint32_t *mine = region + w * kRegion + lane_id() * CPL;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
+    for (int q = 0; q < NW; q++) {
         __attribute__((ext_vector_type(4))) uint32_t t;
         t[0] = c[4 * q];
         t[1] = c[4 * q + 1];
@@ -209,13 +239,20 @@ __global__ __launch_bounds__(kCountThreads) void count_kernel(const uint8_t *map
     const int width = geo_width(g);
     const int rpw = 1 << g.rpw_log2;
     for (int i = (int)threadIdx.x; i < width; i += kCountThreads) {
+        const int col = stripe * width + i;
+        if (col >= g.E)
+            continue;
         uint32_t a = 0;
         for (int ww = 0; ww < kCountWaves; ww++)
             for (int rl = 0; rl < rpw; rl++)
-                a += region[ww * kCountRegion + rl * width + i];
-        const int col = stripe * width + i;
-        if (col < g.E && a)
-            atomicAdd((unsigned long long *)(counts + col), (unsigned long long)a);
+                a += region[ww * kRegion + rl * width + i];
+        const uint64_t add = (1ull << 32) | a;
+        const uint64_t old =
+            __hip_atomic_fetch_add(ws + col, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(old >> 32) == (uint32_t)g.gsplit - 1u) {
+            counts[col] = (int64_t)((uint32_t)old + a);
+            __hip_atomic_store(ws + col, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -329,20 +366,29 @@ unsigned grid_of(const ColGeo &g) { return (unsigned)g.gsplit * (unsigned)g.nstr
 }  // namespace
 
 hipError_t launch_count(const uint8_t *map, int vec, const ColGeo &g, int64_t *counts,
-                        hipStream_t stream)
+                        uint64_t *ws, hipStream_t stream)
 {
-    hipLaunchKernelGGL(zero_counts_kernel, dim3((g.E + kBlock - 1) / kBlock), dim3(kBlock), 0,
-                       stream, counts, g.E);
-    if (g.gsplit > 0) {
-        const dim3 grid(grid_of(g)), block(kCountThreads);
-        if (vec == 16)
-            hipLaunchKernelGGL(count_kernel<16>, grid, block, 0, stream, map, g, counts);
-        else if (vec == 4)
-            hipLaunchKernelGGL(count_kernel<4>, grid, block, 0, stream, map, g, counts);
-        else
-            hipLaunchKernelGGL(count_kernel<1>, grid, block, 0, stream, map, g, counts);
+    if (g.gsplit == 0) {
+        hipLaunchKernelGGL(zero_counts_kernel, dim3((g.E + kBlock - 1) / kBlock), dim3(kBlock), 0,
+                           stream, counts, g.E);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    const dim3 grid(grid_of(g)), block(kCountThreads);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, map, g, counts, ws);
+        return true;
+    };
+    const bool ok =
+        g.cpl_log2 == 4 ? (vec == 16 ? go(count_kernel<16, 16>)
+                           : vec == 8 ? go(count_kernel<16, 8>)
+                           : vec == 4 ? go(count_kernel<16, 4>)
+                                      : go(count_kernel<16, 1>))
+        : g.cpl_log2 == 3 ? (vec == 8 ? go(count_kernel<8, 8>)
+                             : vec == 4 ? go(count_kernel<8, 4>)
+                                        : go(count_kernel<8, 1>))
+        : g.cpl_log2 == 2 ? (vec == 4 ? go(count_kernel<4, 4>) : go(count_kernel<4, 1>))
+                          : false;
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_loss(const void *scores, int dtype, bool vec, const ColGeo &g,

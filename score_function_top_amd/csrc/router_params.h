@@ -148,21 +148,64 @@ constexpr int geo_split_row(const ColGeo &g, int w, int k, int row_lane)
     return ((w + g.waves * k) << g.rpw_log2) + row_lane;
 }
 
-// Count kernel: 8 waves, 16 map bytes per lane and row; loss kernels: 4
+// Count kernel: 8 waves; CPL map bytes per lane and row with CPL the
+// largest of 16, 8 and 4 whose stripes cover E with at most 5% idle columns
+// (else the one that wastes least); row steps per split halved from 16
+// (down to 1) until the grid has kCountMinBlocks blocks.  Loss kernels: 4
 // waves, 4 elements per lane and row.
 constexpr int kCountWaves = 8;
-constexpr int kCountCpl = 4;          // log2 of 16 columns per lane
-constexpr int kCountSteps = 16;       // row steps per wave and split (map)
-constexpr int kCountMaxBlocks = 1024;
+constexpr int kCountMaxSteps = 16;    // row steps per wave and split (map)
+constexpr int kCountMinBlocks = 512;
+constexpr int kCountMaxBlocks = 2048;
 constexpr int kLossWaves = kWaves;
 constexpr int kLossCpl = 2;           // log2 of 4 columns per lane
 constexpr int kLossSteps = 16;        // row steps per wave and split (scores)
 constexpr int kLossMaxBlocks = 4096;
 
+inline int count_cpl_log2(int E)
+{
+    int best = 4;
+    double best_u = -1.0;
+    for (int l = 4; l >= 2; l--) {
+        const ColGeo g = col_geo(1, E, kCountWaves, l, 1, 1);
+        const double u = (double)E / ((double)g.nstripe * geo_width(g));
+        if (u >= 0.95)
+            return l;
+        if (u > best_u) {
+            best_u = u;
+            best = l;
+        }
+    }
+    return best;
+}
+
 inline ColGeo count_geo(int64_t T, int E)
 {
-    return col_geo(T, E, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks);
+    const int cl = count_cpl_log2(E);
+    int steps = kCountMaxSteps;
+    ColGeo g = col_geo(T, E, kCountWaves, cl, steps, kCountMaxBlocks);
+    while (steps > 1 && (int64_t)g.gsplit * g.nstripe < kCountMinBlocks) {
+        steps /= 2;
+        g = col_geo(T, E, kCountWaves, cl, steps, kCountMaxBlocks);
+    }
+    return g;
 }
+
+// Workspace of the count kernel: one 64-bit word per stripe column
+// (contributions received in the high half, routed tokens in the low half),
+// zero before a call and zero again after it (the last contribution to a
+// column hands its total out and clears the word).  Depends on E only.
+inline size_t count_ws_words(int E)
+{
+    const ColGeo g = col_geo(1, E, kCountWaves, count_cpl_log2(E), 1, 1);
+    return (size_t)g.nstripe * geo_width(g);
+}
+inline size_t count_ws_bytes(int E)
+{
+    const size_t n = (count_ws_words(E) * 8 + 255) / 256 * 256;
+    return n < 256 ? 256 : n;
+}
+
 inline ColGeo loss_geo(int64_t T, int E)
 {
     return col_geo(T, E, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks);
@@ -190,10 +233,10 @@ inline size_t aux_ws_bytes(int64_t T, int E)
     return n < 256 ? 256 : n;
 }
 
-// vec: 16 for 16-byte map loads (E % 16 == 0, 16-byte aligned map), 4 for
-// 4-byte loads (E % 4 == 0, 4-byte aligned), else 1 (byte loads).
+// vec: the widest map load (16, 8 or 4 bytes, at most the bytes a lane owns
+// per row) that E and the map's alignment allow, else 1 (byte loads).
 hipError_t launch_count(const uint8_t *map, int vec, const ColGeo &g, int64_t *counts,
-                        hipStream_t stream);
+                        uint64_t *ws, hipStream_t stream);
 hipError_t launch_loss(const void *scores, int dtype, bool vec, const ColGeo &g,
                        const int64_t *counts, double C, double *ws, float *loss,
                        hipStream_t stream);

@@ -8,7 +8,8 @@ fallback: if librouter.so is not built, every call raises.
 
 Entry points carry the C names: router_topk_fwd, router_topk_bwd,
 router_aux_scores, router_aux_scores_bwd, router_tokens_per_expert,
-router_aux_loss_fwd, router_aux_loss_bwd, router_aux_loss_workspace_bytes,
+router_tokens_per_expert_workspace_bytes, router_aux_loss_fwd,
+router_aux_loss_bwd, router_aux_loss_workspace_bytes,
 router_route_maps, router_topk_shared_gate.
 """
 import ctypes
@@ -60,7 +61,9 @@ def load():
     lib.router_aux_loss_workspace_bytes.argtypes = [i64, i32]
     lib.router_aux_loss_workspace_bytes.restype = ctypes.c_size_t
     sz = ctypes.c_size_t
-    lib.router_tokens_per_expert.argtypes = [vp, i64, i32, vp, vp]
+    lib.router_tokens_per_expert.argtypes = [vp, i64, i32, vp, vp, sz, vp]
+    lib.router_tokens_per_expert_workspace_bytes.argtypes = [i64, i32]
+    lib.router_tokens_per_expert_workspace_bytes.restype = ctypes.c_size_t
     lib.router_aux_loss_fwd.argtypes = [vp, ci, i64, i32, vp, i64, i32, f32, vp, vp, sz, vp]
     lib.router_aux_loss_bwd.argtypes = [vp, vp, ci, i64, i32, i64, i32, f32, vp, vp]
     lib.router_route_maps.argtypes = [vp, ci, i32, i32, i32, ci, ci, vp, vp, vp, vp, vp, vp, vp]
@@ -252,9 +255,18 @@ def _counts(c, E, device):
     return c
 
 
-def router_tokens_per_expert(routing_map, out=None):
+def router_tokens_per_expert_workspace_bytes(T, E):
+    """Workspace bytes of router_tokens_per_expert (0 if T, E are out of
+    range)."""
+    return load().router_tokens_per_expert_workspace_bytes(int(T), int(E))
+
+
+def router_tokens_per_expert(routing_map, out=None, workspace=None):
     """Tokens routed to each expert: int64 [E] column counts of the bool (or
-    uint8) routing map [T,E]."""
+    uint8) routing map [T,E].  `workspace`: a device tensor of at least
+    router_tokens_per_expert_workspace_bytes(T, E) bytes that is
+    zero-filled before its first use; every call leaves it zero-filled
+    (without one, a zero-filled one is allocated for the call)."""
     if (not isinstance(routing_map, torch.Tensor) or routing_map.dim() != 2
             or not routing_map.is_cuda or not routing_map.is_contiguous()
             or routing_map.dtype not in (torch.bool, torch.uint8)):
@@ -262,7 +274,14 @@ def router_tokens_per_expert(routing_map, out=None):
     T, E = routing_map.shape
     dev = routing_map.device
     counts = _out(out, (E,), torch.int64, dev, "tokens_per_expert")
+    need = router_tokens_per_expert_workspace_bytes(T, E)
+    if workspace is None:
+        workspace = torch.zeros((max(need, 256),), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the map's device")
     check(load().router_tokens_per_expert(_ptr(routing_map), T, E, _ptr(counts),
+                                          _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
                                           _stream(routing_map)))
     return counts
 

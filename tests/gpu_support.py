@@ -15,10 +15,11 @@ atol 1e-7, bf16 rtol 1e-2):
       - the keys and group values of the two sides agree within the fp32
         relative tolerance of the row's largest one (scale-aware: softmax
         group scores near q/E get a band of that size, not an absolute one);
-      - a row whose map differs from the oracle's must have an oracle margin
-        (gap between the last kept and the first dropped key or group score)
-        below twice the measured key error of that row (no other flip is
-        possible), must keep every group the oracle's scores force
+      - a row whose map differs from the oracle's must be a near-tie row:
+        at the group stage or (with a bias) the expert stage, the oracle's gap
+        between the last kept and the first dropped candidate is below twice
+        that stage's measured error on the row (no other flip is possible;
+        logits are exact keys), and the row must keep every group the oracle's scores force
         (above the (Kg+1)-th score by more than that band) and at most Kg
         groups, must order the experts of those groups within the band, and
         must carry weights consistent with its own selection;
@@ -165,9 +166,11 @@ def decision_inputs(s, x64, bias):
 
 def check_decisions(wl, x64, bias, gpu_map, gpu_inter, S, margin):
     """Decision parity and the key-error bounds of the module doc, for a
-    forward whose selection is decided on computed keys.  Returns the band
-    of every row (twice its larger measured key or group-score error) and
-    the oracle's keys and group values."""
+    forward whose selection is decided on computed keys.  Returns the rows
+    where a stage's gap is within twice that stage's measured error (group
+    scores, or keys with a bias: logits are exact), the band of every row
+    (twice its larger measured error), and the oracle's keys and group
+    values."""
     K = wl.K
     G, Kg = wl.num_groups, wl.group_topk
     # decision parity: the oracle's selection step on the GPU's own keys
@@ -185,6 +188,9 @@ def check_decisions(wl, x64, bias, gpu_map, gpu_inter, S, margin):
     assert (e_key <= F32_RTOL * scale_k).all(), \
         f"{wl.name}: keys differ by {worst:.3g} of the row's largest (> {F32_RTOL})"
     e_grp = np.zeros_like(e_key)
+    T, E = key_o.shape
+    gap_g = np.full(T, np.inf)
+    allowed = np.ones((T, E), bool)
     if G:
         h_g = group_scores32(gv_g.astype(np.float32), G, K // Kg)
         h_o = group_scores32(gv_o.astype(np.float32), G, K // Kg)
@@ -193,7 +199,28 @@ def check_decisions(wl, x64, bias, gpu_map, gpu_inter, S, margin):
         worst = np.max(e_grp / np.maximum(scale_h, 1e-300))
         assert (e_grp <= 2 * F32_RTOL * scale_h).all(), \
             f"{wl.name}: group scores differ by {worst:.3g} of the largest (> {2 * F32_RTOL})"
-    return 2 * np.maximum(e_key, e_grp), key_o, gv_o
+        # the oracle's kept groups (Kg largest scores, ties to the lower
+        # group) and the gap at the group stage
+        order = np.lexsort((np.broadcast_to(np.arange(G), h_o.shape), -h_o), axis=1)
+        hs = np.take_along_axis(h_o, order, 1)
+        if Kg < G:
+            gap_g = hs[:, Kg - 1] - hs[:, Kg]
+        kept = np.zeros((T, G), bool)
+        np.put_along_axis(kept, order[:, :Kg], True, 1)
+        allowed = np.repeat(kept, E // G, axis=1)
+    # the gap at the expert stage, among the oracle's allowed experts
+    ks = -np.sort(-np.where(allowed, key_o, -np.inf), axis=1)
+    gap_e = np.where(np.isfinite(ks[:, K]), ks[:, K - 1] - ks[:, K], np.inf) if K < E \
+        else np.full(T, np.inf)
+    assert (np.minimum(gap_g, gap_e) == margin).all(), "stage gaps disagree with the oracle"
+
+    def flip(gap, band):
+        # a kept and a dropped candidate can swap only if their gap is below
+        # the band, or equals a nonzero band and the tie rule decides
+        return (gap < band) | ((gap == band) & (band > 0))
+
+    near = flip(gap_g, 2 * e_grp) | flip(gap_e, 2 * e_key)
+    return np.nonzero(near)[0], 2 * np.maximum(e_key, e_grp), key_o, gv_o
 
 
 def check_near_tie(rows, band, gpu_map, gpu_probs, S, key_o, gv_o, wl):
@@ -239,10 +266,7 @@ def check_forward(wl, x64, bias, gp, gm, gi, P, M, S, margin):
     differ = np.nonzero((gm != M).any(1))[0]
     near = np.zeros(0, int)
     if bias is not None or wl.num_groups > 0:
-        band, key_o, gv_o = check_decisions(wl, x64, bias, gm, gi, S, margin)
-        # a kept and a dropped candidate can swap only if their gap is below
-        # the band, or equals a nonzero band and the tie rule decides
-        near = np.nonzero((margin < band) | ((margin == band) & (band > 0)))[0]
+        near, band, key_o, gv_o = check_decisions(wl, x64, bias, gm, gi, S, margin)
         outside = np.setdiff1d(differ, near)
         assert outside.size == 0, (
             f"{wl.name}: routing map differs on {outside.size} rows whose oracle margin "

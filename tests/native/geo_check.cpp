@@ -5,7 +5,10 @@
 // other access is masked (column >= E) or past its split's buffer, that
 // byte offsets fit the 32-bit buffer offsets, that the LDS column index of
 // the count kernel stays within its array, and that the loss workspace fits
-// the queried size (the forward's geometry; the gradient's writes only).
+// the queried size (the forward's geometry; the gradient's writes only);
+// for the count geometry also that the lane width and row steps are the
+// ones the kernel is built for, that the accumulators and tickets fit the
+// queried workspace, and that the workspace bound holds for every E.
 // Prints "ok" or the first failure; exit status 0/1.
 #include <cstdio>
 #include <cstdlib>
@@ -95,8 +98,31 @@ static int check(int64_t T, int E, int waves, int cpl_log2, int steps, int max_b
     return 0;
 }
 
+// The count kernel's geometry for (T, E), walked like the others, plus its
+// workspace: a 64-bit accumulator for each of nstripe*width columns inside
+// count_ws_bytes(E) <= 65536 bytes, and contribution counts (gsplit per
+// column) that fit the accumulator's high half.
+static int check_count(int64_t T, int E)
+{
+    const ColGeo g = count_geo(T, E);
+    if (g.cpl_log2 < 2 || g.cpl_log2 > 4 || g.steps < 1 || g.steps > kCountMaxSteps ||
+        (g.steps & (g.steps - 1)) != 0)
+        return fail("count lane width / steps", T, E, g.steps);
+    const size_t words = (size_t)g.nstripe * geo_width(g);
+    if (words > count_ws_words(E) || count_ws_words(E) * 8 > count_ws_bytes(E) ||
+        count_ws_bytes(E) > 65536 || count_ws_bytes(E) % 256 != 0)
+        return fail("count workspace", T, E, g.steps);
+    if (T > 0 && (int64_t)g.gsplit * g.nstripe > (kCountMaxBlocks > g.nstripe ? kCountMaxBlocks
+                                                                                : g.nstripe))
+        return fail("count grid", T, E, g.steps);
+    return check(T, E, kCountWaves, g.cpl_log2, g.steps, kCountMaxBlocks, 1);
+}
+
 int main()
 {
+    for (int E = 1; E <= 4096; E++)
+        if (check_count(1, E))
+            return 1;
     const int64_t Ts[] = {0, 1, 3, 64, 127, 128, 129, 1031, 4096, 8192, 20000};
     const int Es[] = {1, 2, 3, 4, 5, 7, 8, 16, 60, 64, 100, 128, 255, 256, 257,
                       512, 999, 1000, 2304, 4095, 4096};
@@ -105,7 +131,7 @@ int main()
         for (int E : Es) {
             if (T * E > 40000000)
                 continue;
-            bad |= check(T, E, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks, 1);
+            bad |= check_count(T, E);
             bad |= check(T, E, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks, 4);
             bad |= check(T, E, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks, 2);
             bad |= check(T, E, kLossWaves, kLossCpl, kLossBwdSteps, kLossBwdMaxBlocks, 4);
@@ -114,8 +140,9 @@ int main()
                 return 1;
         }
     // grid cap reached: blocks loop over several splits
-    bad |= check(300000, 64, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks, 1);
-    bad |= check(40000, 2304, kCountWaves, kCountCpl, kCountSteps, kCountMaxBlocks, 1);
+    bad |= check_count(300000, 64);
+    bad |= check_count(40000, 2304);
+    bad |= check_count(70000, 4096);
     bad |= check(70000, 2304, kLossWaves, kLossCpl, kLossSteps, kLossMaxBlocks, 4);
     bad |= check(100000, 4, kLossWaves, kLossCpl, kLossSteps, 64, 4);
     bad |= check(40000, 2304, kLossWaves, kLossCpl, kLossBwdSteps, kLossBwdMaxBlocks, 4);

@@ -67,10 +67,19 @@ def run_loss(T, E, K, seed, dtype=synth.F32, N=None, coeff=COEFF, counts=None, v
 
 # ------------------------------------------------------------------ counts
 
+# Shapes cover every lane width and load width of the count kernel: 16
+# map bytes per lane with 16-, 8-, 4- and 1-byte loads (E = 4096, 1000,
+# 100, 999), 8 (E = 1536 with 8-byte loads, 1532 with 4-byte, 5 with byte
+# loads), 4 (E = 2304, 1540 with 4-byte loads; 1537 and 1 with byte loads),
+# and grids from 1 to 2048 blocks (the cap makes blocks loop over several
+# row splits at T = 300000 and 70000).
 @pytest.mark.parametrize("T,E,K", [(64, 16, 2), (8192, 256, 4), (8192, 512, 22),
                                    (8192, 2304, 36), (1031, 999, 7), (129, 5, 2),
                                    (1, 1, 1), (3, 4096, 100), (40000, 2304, 36),
-                                   (300000, 64, 6)])
+                                   (300000, 64, 6), (8192, 4096, 16), (4099, 1000, 9),
+                                   (2000, 100, 3), (3001, 1536, 12), (3001, 1532, 12),
+                                   (2500, 1540, 8), (2500, 1537, 8), (16384, 256, 8),
+                                   (70000, 2304, 36)])
 def test_tokens_per_expert(T, E, K):
     say(f"[counts] T={T} E={E} K={K}")
     m = synth.random_map(7000 + E + K, T, E, K)
@@ -98,6 +107,24 @@ def test_tokens_per_expert_zero_rows_and_stale_output():
     m = synth.random_map(72, 4099, 300, 9)
     out = torch.full((300,), 123456, dtype=torch.int64, device=DEV)
     assert (gpu_counts(m, out=out) == oracle.tokens_per_expert(m)).all()
+
+
+def test_tokens_per_expert_workspace_reuse():
+    """One zero-filled workspace serves a run of calls of different shapes
+    (stream-ordered); each call leaves it zero-filled again."""
+    ws = torch.zeros((router.router_tokens_per_expert_workspace_bytes(1, 4096),),
+                     dtype=torch.uint8, device=DEV)
+    for i, (T, E, K) in enumerate([(8192, 2304, 36), (513, 64, 5), (8192, 2304, 36),
+                                   (4099, 4096, 30), (1, 7, 1), (16384, 256, 8)]):
+        say(f"[counts reuse] T={T} E={E}")
+        m = synth.random_map(7400 + i, T, E, K)
+        t = torch.from_numpy(m).to(DEV)
+        c = router.router_tokens_per_expert(t, workspace=ws)
+        c2 = router.router_tokens_per_expert(t, workspace=ws)
+        torch.cuda.synchronize()
+        want = oracle.tokens_per_expert(m)
+        assert (c.cpu().numpy() == want).all() and (c2.cpu().numpy() == want).all(), (T, E)
+        assert int(ws.count_nonzero()) == 0, "workspace not returned zero-filled"
 
 
 def test_tokens_per_expert_unaligned_view():
@@ -214,17 +241,20 @@ def test_aux_loss_chain_from_logits():
 
 def test_aux_loss_graph_replay():
     """Counts and loss captured in a HIP graph and replayed several times,
-    with eager work between replays (the outputs cleared and the workspace
-    refilled), match the eager results each time."""
+    with eager work between replays (the outputs cleared and the loss
+    workspace refilled), match the eager results each time; the count
+    workspace is zero-filled after every replay."""
     T, E, K = 4096, 512, 8
     st, _ = synth.prob_like(7600, T, E)
     s = to_dev(st, synth.F32)
     m = torch.from_numpy(synth.random_map(7601, T, E, K)).to(DEV)
     ws = torch.empty((router.router_aux_loss_workspace_bytes(T, E),), dtype=torch.uint8,
                      device=DEV)
+    cws = torch.zeros((router.router_tokens_per_expert_workspace_bytes(T, E),),
+                      dtype=torch.uint8, device=DEV)
     cnt = torch.empty((E,), dtype=torch.int64, device=DEV)
     loss = torch.empty((), dtype=torch.float32, device=DEV)
-    router.router_tokens_per_expert(m, out=cnt)
+    router.router_tokens_per_expert(m, out=cnt, workspace=cws)
     router.router_aux_loss_fwd(s, cnt, T, K, COEFF, out=loss, workspace=ws)
     torch.cuda.synchronize()
     want_c, want_l = cnt.clone(), loss.clone()
@@ -233,7 +263,7 @@ def test_aux_loss_graph_replay():
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            router.router_tokens_per_expert(m, out=cnt)
+            router.router_tokens_per_expert(m, out=cnt, workspace=cws)
             router.router_aux_loss_fwd(s, cnt, T, K, COEFF, out=loss, workspace=ws)
     torch.cuda.synchronize()
     for i in range(4):
@@ -244,3 +274,4 @@ def test_aux_loss_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(cnt, want_c) and torch.equal(loss, want_l), i
+        assert int(cws.count_nonzero()) == 0, i

@@ -195,18 +195,34 @@ def test_aux_loss_workspace_query():
     assert f(-1, 8) == 0 and f(8, 0) == 0 and f(8, 4097) == 0 and f(1 << 62, 16) == 0
 
 
+def test_tokens_per_expert_workspace_query():
+    f = router.router_tokens_per_expert_workspace_bytes
+    for E in (1, 16, 100, 256, 999, 1536, 2304, 4095, 4096):
+        n = f(8192, E)
+        assert n >= 256 and n % 256 == 0 and n <= 65536 and n >= 8 * E, E
+        assert f(0, E) == n and f(1 << 20, E) == n        # depends on E only
+    assert f(-1, 8) == 0 and f(8, 0) == 0 and f(8, 4097) == 0 and f(1 << 62, 16) == 0
+
+
 def test_aux_loss_host_checks():
     lib = router.load()
     ws = router.router_aux_loss_workspace_bytes(8, 16)
+    cws = router.router_tokens_per_expert_workspace_bytes(8, 16)
     tpe = lib.router_tokens_per_expert
-    assert tpe(P, 8, 0, P, None) == INV
-    assert tpe(P, -1, 16, P, None) == INV
-    assert tpe(P, 8, 4097, P, None) == UNS
-    assert tpe(P, 1 << 32, 16, P, None) == UNS
-    assert tpe(P, 1 << 62, 16, P, None) == OVF
-    assert tpe(None, 8, 16, P, None) == INV
-    assert tpe(P, 8, 16, None, None) == INV
-    assert tpe(P, 8, 16, P + 4, None) == INV              # counts not 8-byte aligned
+
+    def count(m=P, T=8, E=16, n=P, w=P, wb=cws):
+        return tpe(m, T, E, n, w, wb, None)
+    assert count(E=0) == INV
+    assert count(T=-1) == INV
+    assert count(E=4097) == UNS
+    assert count(T=1 << 32) == UNS
+    assert count(T=1 << 62) == OVF
+    assert count(m=None) == INV
+    assert count(n=None) == INV
+    assert count(n=P + 4) == INV                          # counts not 8-byte aligned
+    assert count(w=None) == INV
+    assert count(w=P + 4) == INV                          # workspace not 8-byte aligned
+    assert count(wb=cws - 8) == INV                       # workspace too small
     fwd = lib.router_aux_loss_fwd
     good = dict(s=P, dtype=0, T=8, E=16, n=P, N=8, K=2, c=0.01, loss=P, ws=P, wsb=ws)
 

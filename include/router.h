@@ -227,6 +227,29 @@ router_status router_aux_loss_fwd(const void *scores, int dtype, int64_t T,
                                   size_t workspace_bytes, void *hip_stream);
 
 /*
+ * router_aux_loss_fwd_noalloc -- router_aux_loss_fwd without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The same kernels and the same result, bit for bit; the per-block partial
+ * sums go to a buffer of ROUTER_AUX_LOSS_SCRATCH_BYTES that the library
+ * holds in device memory on every GPU it runs on (until the process ends).
+ * The call allocates nothing.  Calls on one GPU share that buffer, so calls
+ * that may overlap on one GPU (other streams, other threads) race and must
+ * not be issued; stream-ordered calls are fine.  Errors as
+ * router_aux_loss_fwd; shapes whose partials exceed the buffer return
+ * ROUTER_ERR_UNSUPPORTED (none with E <= ROUTER_MAX_EXPERTS: the partials
+ * take at most 32768 bytes); ROUTER_ERR_HIP if the buffer's device address
+ * cannot be found.
+ */
+#define ROUTER_AUX_LOSS_SCRATCH_BYTES 32768
+router_status router_aux_loss_fwd_noalloc(const void *scores, int dtype,
+                                          int64_t T, int32_t E,
+                                          const int64_t *tokens_per_expert,
+                                          int64_t total_tokens, int32_t K,
+                                          float coeff, float *loss,
+                                          void *hip_stream);
+
+/*
  * router_aux_loss_bwd -- grad_scores [T,E] (`dtype`) =
  * grad_loss[0] * coeff * E * n_i / (N^2 K), with grad_loss one fp32 on the
  * device (the upstream gradient of the loss).  Arguments and errors as

@@ -22,6 +22,9 @@
 
 using namespace rker;
 
+static_assert(ROUTER_AUX_LOSS_SCRATCH_BYTES == kLossScratchBytes,
+              "the header states the library's loss buffer size");
+
 namespace {
 
 // ------------------------------------------------------------ threshold
@@ -479,6 +482,33 @@ router_status router_aux_loss_fwd(const void *scores, int dtype, int64_t T, int3
     const hipError_t e =
         launch_loss(scores, dtype, vec, loss_geo(T, E), tokens_per_expert,
                     loss_coeff(coeff, E, total_tokens, K), (double *)workspace, loss,
+                    (hipStream_t)hip_stream);
+    return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+}
+
+router_status router_aux_loss_fwd_noalloc(const void *scores, int dtype, int64_t T, int32_t E,
+                                          const int64_t *tokens_per_expert, int64_t total_tokens,
+                                          int32_t K, float coeff, float *loss, void *hip_stream)
+{
+    router_status st = check_loss_shape(T, E);
+    if (st == ROUTER_OK)
+        st = check_loss_args(dtype, total_tokens, K, coeff);
+    if (st != ROUTER_OK)
+        return st;
+    if (!tokens_per_expert || !loss || (T > 0 && !scores))
+        return ROUTER_ERR_INVALID_ARG;
+    const size_t ds = dsize(dtype);
+    if (!aligned(scores, ds) || !aligned(tokens_per_expert, 8) || !aligned(loss, 4))
+        return ROUTER_ERR_INVALID_ARG;
+    if (aux_ws_bytes(T, E) > kLossScratchBytes)
+        return ROUTER_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (loss_scratch(&ws) != hipSuccess)
+        return ROUTER_ERR_HIP;
+    const bool vec = E % 4 == 0 && aligned(scores, 4 * ds);
+    const hipError_t e =
+        launch_loss(scores, dtype, vec, loss_geo(T, E), tokens_per_expert,
+                    loss_coeff(coeff, E, total_tokens, K), (double *)ws, loss,
                     (hipStream_t)hip_stream);
     return e == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }

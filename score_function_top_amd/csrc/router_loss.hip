@@ -21,6 +21,7 @@
 // the last block of each column stripe writes them out (one launch).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "router_io.h"
@@ -389,6 +390,35 @@ hipError_t launch_count(const uint8_t *map, int vec, const ColGeo &g, int64_t *c
         : g.cpl_log2 == 2 ? (vec == 4 ? go(count_kernel<4, 4>) : go(count_kernel<4, 1>))
                           : false;
     return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+// Device memory the library owns for router_aux_loss_fwd_noalloc: the loss
+// kernel's per-block fp64 partial sums, for callers that cannot allocate.
+// Every GPU the library runs on holds its own copy until the process ends;
+// calls on one GPU share it (their contents need no clearing: every partial
+// is written before it is read, in stream order), so calls that overlap on
+// one GPU race.  Host code uses the per-device address hipGetSymbolAddress
+// returns, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kLossScratchBytes];
+
+hipError_t loss_scratch(void **ptr)
+{
+    constexpr int kMaxDev = 64;
+    static std::once_flag once[kMaxDev];
+    static void *addr[kMaxDev];
+    static hipError_t err[kMaxDev];
+    int d = 0;
+    const hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess)
+        return e;
+    if (d < 0 || d >= kMaxDev)
+        return hipErrorInvalidDevice;
+    // looked up once per device, with that device current
+    std::call_once(once[d], [&] { err[d] = hipGetSymbolAddress(&addr[d], HIP_SYMBOL(scratch)); });
+    if (err[d] != hipSuccess)
+        return err[d];
+    *ptr = addr[d];
+    return hipSuccess;
 }
 
 hipError_t launch_loss(const void *scores, int dtype, bool vec, const ColGeo &g,

@@ -240,6 +240,10 @@ hipError_t launch_count(const uint8_t *map, int vec, const ColGeo &g, int64_t *c
 hipError_t launch_loss(const void *scores, int dtype, bool vec, const ColGeo &g,
                        const int64_t *counts, double C, double *ws, float *loss,
                        hipStream_t stream);
+// The library's own loss workspace (per device, kLossScratchBytes): its
+// device address on the current device.
+constexpr size_t kLossScratchBytes = 32768;
+hipError_t loss_scratch(void **ptr);
 hipError_t launch_loss_bwd(const float *grad_loss, const int64_t *counts, int dtype, bool vec,
                            const ColGeo &g, double C, void *grad_scores, hipStream_t stream);
 

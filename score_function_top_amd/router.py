@@ -9,7 +9,7 @@ fallback: if librouter.so is not built, every call raises.
 Entry points carry the C names: router_topk_fwd, router_topk_bwd,
 router_aux_scores, router_aux_scores_bwd, router_tokens_per_expert,
 router_tokens_per_expert_workspace_bytes, router_aux_loss_fwd,
-router_aux_loss_bwd, router_aux_loss_workspace_bytes,
+router_aux_loss_fwd_noalloc, router_aux_loss_bwd, router_aux_loss_workspace_bytes,
 router_route_maps, router_topk_shared_gate.
 """
 import ctypes
@@ -66,6 +66,8 @@ def load():
     lib.router_tokens_per_expert_workspace_bytes.restype = ctypes.c_size_t
     lib.router_aux_loss_fwd.argtypes = [vp, ci, i64, i32, vp, i64, i32, f32, vp, vp, sz, vp]
     lib.router_aux_loss_bwd.argtypes = [vp, vp, ci, i64, i32, i64, i32, f32, vp, vp]
+    lib.router_aux_loss_fwd_noalloc.argtypes = [vp, ci, i64, i32, vp, i64, i32, f32, vp, vp]
+    lib.router_aux_loss_fwd_noalloc.restype = ci
     lib.router_route_maps.argtypes = [vp, ci, i32, i32, i32, ci, ci, vp, vp, vp, vp, vp, vp, vp]
     lib.router_route_maps.restype = ci
     lib.router_topk_shared_gate.argtypes = [vp, vp, vp, ci, i64, i32, i32, i32, i32, ci, f32,
@@ -299,6 +301,20 @@ def router_aux_loss_fwd(scores, tokens_per_expert, total_tokens, topk, coeff,
         _ptr(scores), _DTYPE[scores.dtype], T, E, _ptr(counts), int(total_tokens),
         int(topk), float(coeff), _ptr(loss), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(scores)))
+    return loss
+
+
+def router_aux_loss_fwd_noalloc(scores, tokens_per_expert, total_tokens, topk, coeff, out):
+    """router_aux_loss_fwd into a preallocated 0-dim float32 `out`, with the
+    library's own scratch buffer instead of a workspace: allocates nothing
+    (for callers that cannot allocate); calls that overlap on one GPU race."""
+    T, E = _rows(scores, "scores")
+    dev = scores.device
+    counts = _counts(tokens_per_expert, E, dev)
+    loss = _out(out, (), torch.float32, dev, "loss")
+    check(load().router_aux_loss_fwd_noalloc(
+        _ptr(scores), _DTYPE[scores.dtype], T, E, _ptr(counts), int(total_tokens), int(topk),
+        float(coeff), _ptr(loss), _stream(scores)))
     return loss
 
 

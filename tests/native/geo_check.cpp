@@ -42,7 +42,7 @@ static int check(int64_t T, int E, int waves, int cpl_log2, int steps, int max_b
     const size_t ws = aux_ws_bytes(T, E);
     const bool loss = waves == kLossWaves && cpl_log2 == kLossCpl && steps == kLossSteps &&
                       max_blocks == kLossMaxBlocks;
-    if (loss && (size_t)g.gsplit * g.nstripe * 8 > ws)
+    if (loss && ((size_t)g.gsplit * g.nstripe * 8 > ws || ws > kLossScratchBytes))
         return fail("loss workspace", T, E, steps);
     std::vector<uint8_t> seen((size_t)T * E, 0);
     const unsigned grid = (unsigned)g.gsplit * (unsigned)g.nstripe;
@@ -120,6 +120,12 @@ static int check_count(int64_t T, int E)
 
 int main()
 {
+    // the loss partials fit the library's own buffer for every E (any T:
+    // the grid is capped)
+    for (int E = 1; E <= 4096; E++)
+        for (int64_t T : {(int64_t)1, (int64_t)8192, (int64_t)1 << 20, (int64_t)1 << 31})
+            if (aux_ws_bytes(T, E) > kLossScratchBytes)
+                return fail("loss partials past the library's buffer", T, E, 0);
     for (int E = 1; E <= 4096; E++)
         if (check_count(1, E))
             return 1;

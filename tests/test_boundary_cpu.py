@@ -238,6 +238,19 @@ def test_aux_loss_host_checks():
                    (dict(ws=None), INV), (dict(wsb=ws - 8), INV), (dict(s=P + 2), INV),
                    (dict(dtype=1, s=P + 1), INV), (dict(loss=P + 2), INV)):
         assert call(**kw) == st, kw
+    na = lib.router_aux_loss_fwd_noalloc
+
+    def call_na(**kw):
+        a = dict(good)
+        a.update(kw)
+        return na(a["s"], a["dtype"], a["T"], a["E"], a["n"], a["N"], a["K"], a["c"],
+                  a["loss"], None)
+    for kw, st in ((dict(dtype=2), INV), (dict(T=-1), INV), (dict(E=0), INV),
+                   (dict(E=5000), UNS), (dict(T=1 << 62), OVF), (dict(N=0), INV),
+                   (dict(K=0), INV), (dict(c=float("nan")), INV), (dict(s=None), INV),
+                   (dict(n=None), INV), (dict(loss=None), INV), (dict(s=P + 2), INV),
+                   (dict(n=P + 4), INV), (dict(loss=P + 2), INV)):
+        assert call_na(**kw) == st, kw
     bwd = lib.router_aux_loss_bwd
     assert bwd(P, P, 0, 8, 16, 0, 2, 0.01, P, None) == INV     # N = 0
     assert bwd(P, P, 0, 8, 16, 8, 0, 0.01, P, None) == INV     # K = 0

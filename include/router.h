@@ -97,12 +97,26 @@ typedef enum { ROUTER_SOFTMAX = 0, ROUTER_SIGMOID = 1 } router_score_fn;
  *   intermediate = s for every expert (fp32).
  * expert_bias ([E] fp32, or NULL) affects the selection only, and is only
  * accepted with the sigmoid (else ROUTER_ERR_UNSUPPORTED).
- * Checks: T >= 0; 1 <= E <= ROUTER_MAX_EXPERTS (larger E: UNSUPPORTED);
- * 1 <= K <= E; num_groups >= 0; with num_groups > 0: E % num_groups == 0,
- * 1 <= group_topk <= num_groups, K % group_topk == 0 and
- * K / group_topk <= E / num_groups; scaling_factor finite; known dtype and
- * score_fn; non-NULL arrays when T > 0.
+ * Checks (INVALID_ARG): T >= 0; E >= 1; 1 <= K <= E; num_groups >= 0;
+ * with num_groups > 0: E % num_groups == 0, 1 <= group_topk <= num_groups,
+ * K % group_topk == 0 and K / group_topk <= E / num_groups; scaling_factor
+ * finite; known dtype and score_fn; non-NULL arrays when T > 0.
+ * Not implemented (UNSUPPORTED), all decided on the host before any
+ * launch: E > ROUTER_MAX_EXPERTS; expert_bias with the softmax;
+ * num_groups > ROUTER_MAX_GROUPS (one lane of a 64-lane token scores each
+ * group); and, with num_groups > 0, E + num_groups >
+ * ROUTER_GROUP_LDS_MAX_E_PLUS_G: where the group stage keeps a copy of the
+ * row in LDS (groups that are not 4*2^k experts, K / group_topk > 4, rows
+ * of more than 1024 experts, unaligned arrays, or
+ * router_set_group_stage(ROUTER_GROUP_STAGE_LDS)) the copy and the
+ * candidate lists must fit the 64 KB of LDS a workgroup gets, and they do
+ * exactly when E + num_groups <= 3648.  (A device with less LDS per
+ * workgroup than 64 KB would also return UNSUPPORTED, after the device
+ * query.)  The bound follows the fused-router page, "Hardening" (host-side
+ * checks, and the device's shared-memory limit in the buffer decision).
  */
+#define ROUTER_MAX_GROUPS 64
+#define ROUTER_GROUP_LDS_MAX_E_PLUS_G 3648
 router_status router_topk_fwd(const void *logits, int dtype, int64_t T,
                               int32_t E, int32_t K, int score_fn, int renorm,
                               int32_t num_groups, int32_t group_topk,
@@ -372,11 +386,13 @@ router_status router_device_query(int32_t *compute_units, int32_t *clock_khz,
 
 /*
  * Group stage of the group-limited forward.  Passage: the fused-router
- * page, "Forward kernels" (group-limited routing inside the fused kernel).
+ * page, "Hardening" (group-limited routing: topk divisible by group_topk,
+ * and the shared-memory limit that decides how a kernel buffers its data).
  * ROUTER_GROUP_STAGE_AUTO (default) scores the groups in registers when
  * each group of E/num_groups experts is 4*L experts with L a power of two
  * that fits the kernel's lane layout, and through an LDS scratch copy of
- * the row otherwise; ROUTER_GROUP_STAGE_LDS always takes the LDS copy.
+ * the row otherwise; ROUTER_GROUP_STAGE_LDS always takes the LDS copy
+ * (and with it the bound E + num_groups <= ROUTER_GROUP_LDS_MAX_E_PLUS_G).
  * Both give the same scores, maps and outputs.  A process-wide setting;
  * other values return ROUTER_ERR_INVALID_ARG.
  */

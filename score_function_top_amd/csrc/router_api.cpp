@@ -24,6 +24,11 @@ using namespace rker;
 
 static_assert(ROUTER_AUX_LOSS_SCRATCH_BYTES == kLossScratchBytes,
               "the header states the library's loss buffer size");
+// 64-lane tokens, 4 per workgroup: candidate lists plus the row copy of the
+// LDS group stage, (E + G + 64) floats per token
+static_assert((kFwdLdsBytes - 4 * cand_slots(64) * 8) / 16 - 64 == ROUTER_GROUP_LDS_MAX_E_PLUS_G,
+              "the header states the LDS bound of grouped routing");
+static_assert(ROUTER_MAX_GROUPS == 64, "one lane of a 64-lane token per group");
 
 namespace {
 
@@ -245,7 +250,7 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
         return ROUTER_ERR_INVALID_ARG;
     if (bias && score_fn != ROUTER_SIGMOID)
         return ROUTER_ERR_UNSUPPORTED;
-    if (G > 64)
+    if (G > ROUTER_MAX_GROUPS)
         return ROUTER_ERR_UNSUPPORTED;
     if (T == 0)
         return ROUTER_OK;
@@ -282,13 +287,18 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
                      group_reg_log(c, E, G, K / Kg) >= 0;
     const int gm = G == 0 ? GROUP_NONE : (reg ? GROUP_REG : GROUP_LDS);
 
-    DevInfo dev;
-    if (dev_info(&dev) != hipSuccess)
-        return ROUTER_ERR_HIP;
+    // LDS of the launch: the candidate lists, plus the row copy of the LDS
+    // group stage; a host-side bound first (the workgroup LDS the kernels
+    // are built for), then the device's own limit
     const int tpb = kWaves * (64 / c.lpt);
     size_t smem = (size_t)tpb * cand_slots(c.lpt) * sizeof(uint64_t);
     if (gm == GROUP_LDS)
         smem += (size_t)tpb * group_scratch_floats(E, G, c.lpt) * sizeof(float);
+    if (smem > kFwdLdsBytes)
+        return ROUTER_ERR_UNSUPPORTED;
+    DevInfo dev;
+    if (dev_info(&dev) != hipSuccess)
+        return ROUTER_ERR_HIP;
     if (smem > dev.lds_per_block)
         return ROUTER_ERR_UNSUPPORTED;
 

@@ -72,6 +72,10 @@ struct BwdParams {
 // LDS per token group: cand_slots u64 candidate slots; the LDS group stage
 // adds group_scratch_floats floats.
 constexpr int cand_slots(int lpt) { return 3 * lpt; }
+// Workgroup LDS the forward kernels may use (the 64 KB every gfx9 device
+// gives a workgroup); with the LDS group stage at 64 lanes per token this
+// bounds E + G by 3648 (6144 bytes of candidates plus 16 (E + G + 64)).
+constexpr size_t kFwdLdsBytes = 65536;
 constexpr int group_scratch_floats(int E, int G, int lpt)
 {
     return E + G + lpt;

@@ -194,6 +194,19 @@ def test_groups(T, E, K, G, Kg, dtype, biased):
     run_fwd(wl)
 
 
+@pytest.mark.parametrize("E,G,Kg,K,b", [(3640, 8, 2, 4, 0.05), (3584, 64, 4, 8, 0.0)])
+def test_group_lds_bound(E, G, Kg, K, b):
+    """Grouped rows exactly at the LDS bound of the group stage
+    (E + G = 3648) run and match the oracle; one more expert per group
+    is rejected on the host."""
+    wl = edge_wl(70, E, K, synth.SIGMOID, True, bias=b, G=G, Kg=Kg, c=2.5, seed=31)
+    run_fwd(wl)
+    x = torch.zeros((4, E + G), device=DEV)
+    with pytest.raises(router.RouterError) as e:
+        router.router_topk_fwd(x, K, "sigmoid", True, G, Kg)
+    assert e.value.status == router.ERR_UNSUPPORTED
+
+
 def _random_cases(n=48, seed=2024):
     """Seeded random router configurations around the size boundaries of
     the launch plans (lanes per token, chunk counts, selection paths, both

@@ -22,7 +22,7 @@ ARCH = os.environ.get("ROUTER_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["router_api.cpp", "router_lpt16.hip", "router_lpt32.hip",
            "router_lpt64a.hip", "router_lpt64b.hip", "router_lpt64c.hip",
            "router_scalar.hip", "router_loss.hip", "router_route.hip",
-           "router_gate.hip"]
+           "router_gate.hip", ("router_grouped.hip", 16), ("router_grouped.hip", 32)]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms (v_pk_*_f32) stay off: hipcc otherwise
@@ -33,8 +33,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 
 def _compile(src):
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    # a source is a file name, or (file name, lanes) for the grouped kernels,
+    # compiled once per lane width
+    lpt = None
+    if isinstance(src, tuple):
+        src, lpt = src
+    stem = os.path.splitext(src)[0] + ("" if lpt is None else f"_lpt{lpt}")
+    out = os.path.join(OBJ, stem + ".o")
+    defs = [] if lpt is None else [f"-DROUTER_GROUPED_LPT={lpt}"]
+    cmd = ["hipcc", *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -29,6 +29,8 @@ static_assert(ROUTER_AUX_LOSS_SCRATCH_BYTES == kLossScratchBytes,
 static_assert((kFwdLdsBytes - 4 * cand_slots(64) * 8) / 16 - 64 == ROUTER_GROUP_LDS_MAX_E_PLUS_G,
               "the header states the LDS bound of grouped routing");
 static_assert(ROUTER_MAX_GROUPS == 64, "one lane of a 64-lane token per group");
+static_assert(ROUTER_MAX_EXPERTS + ROUTER_MAX_GROUPS <= ROUTER_GROUP_LDS_MAX_E_PLUS_G,
+              "every grouped shape within the other limits fits the LDS");
 
 namespace {
 
@@ -198,6 +200,21 @@ int group_reg_log(const Cfg &c, int E, int G, int q)
     return group_reg_ok(c.lpt, c.nch, lg) ? lg : -1;
 }
 
+// Lanes per token of the kernel for rows of 32-expert groups
+// (router_grouped.h) in the layout c the general path chose, so both group
+// stages share their layout and reduction order: E = 32 * G with G a power
+// of two in [2, 16], q = K / Kg <= 4, a vector layout of 16 or 32 lanes
+// with E = nch * 4 * lanes, and at most one selected expert per lane
+// (K <= lanes); 0 when it does not take the shape.
+int grouped_lpt(const Cfg &c, int E, int G, int K, int Kg)
+{
+    if (G < 2 || G > 16 || E != 32 * G || (G & (G - 1)) != 0 || K / Kg > 4)
+        return 0;
+    if (!c.vec || (c.lpt != 16 && c.lpt != 32) || E != c.nch * 4 * c.lpt || K > c.lpt)
+        return 0;
+    return c.lpt;
+}
+
 hipError_t launch_fwd(const Cfg &c, int dtype, int score, int gm, const FwdParams &p,
                       const Launch &l)
 {
@@ -282,6 +299,42 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     if (sel == SEL_PRUNE && K > (prune_top2(c.lpt, G > 0 ? GROUP_LDS : GROUP_NONE) ? 2 * c.lpt
                                                                                   : c.lpt))
         sel = SEL_BITS;
+
+    // rows of 32-expert groups (E = 64..512) have their own kernel
+    if (g_group_stage.load() == ROUTER_GROUP_STAGE_AUTO && G > 0 && vec) {
+        const int lg = grouped_lpt(c, E, G, K, Kg);
+        if (lg > 0) {
+            DevInfo dev;
+            if (dev_info(&dev) != hipSuccess)
+                return ROUTER_ERR_HIP;
+            const int tpb = kWaves * (64 / lg);
+            FwdParams p{};
+            p.x = x;
+            p.out = out;
+            p.map = map;
+            p.inter = inter;
+            p.bias = bias;
+            p.T = T;
+            p.E = E;
+            p.K = K;
+            p.sel = SEL_PRUNE;
+            p.renorm = renorm ? 1 : 0;
+            p.G = G;
+            p.Kg = Kg;
+            p.q = K / Kg;
+            p.P = E / G;
+            p.scale = scale;
+            const Launch l{grid_for(T, lg), (size_t)tpb * cand_slots(lg) * sizeof(uint64_t),
+                           (hipStream_t)stream};
+            const int nch = c.nch;
+            const int Q = p.q <= 2 ? 2 : 4;
+            hipError_t err = hipErrorInvalidValue;
+            if (!fwd_grouped16(lg, nch, dtype, score_fn, Q, bias != nullptr, p, l, &err) &&
+                !fwd_grouped32(lg, nch, dtype, score_fn, Q, bias != nullptr, p, l, &err))
+                return ROUTER_ERR_HIP;
+            return err == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
+        }
+    }
 
     const bool reg = g_group_stage.load() == ROUTER_GROUP_STAGE_AUTO && G > 0 &&
                      group_reg_log(c, E, G, K / Kg) >= 0;

@@ -352,9 +352,11 @@ __device__ __forceinline__ float ord_key_inv(uint32_t k)
 // product y*log2(e) carried in two parts (the second, from an FMA, holds the
 // rounding error of the first and the tail of the constant) and folded back
 // by 2^t ~ 1 + t ln 2.  y below -200 (padding: -inf) gives exactly 0.
+// The lower clamp is an IEEE maximum (one instruction; fmaxf would first
+// canonicalise its input): the same value for every non-NaN y.
 __device__ __forceinline__ float exp_split(float y)
 {
-    y = fmaxf(y, -200.0f);
+    y = __builtin_elementwise_maximum(y, -200.0f);
     const float L = 1.44269502162933349609375f;       // log2(e) rounded to fp32
     const float Llo = 1.925963033500011079e-8f;       // log2(e) - L
     const float th = y * L;
@@ -365,9 +367,17 @@ __device__ __forceinline__ float exp_split(float y)
 
 // Logistic sigmoid 1 / (1 + e^-x) with the hardware reciprocal (~3 ulp);
 // for x < -88 the result is below 1e-38 instead of the exact tiny value.
+// The exponent -x is clamped to [-200, 88] by one median-of-three (the two
+// clamps of exp_split's domain in one instruction; the same value).
 __device__ __forceinline__ float sigmoid_fast(float x)
 {
-    return __builtin_amdgcn_rcpf(1.0f + exp_split(fminf(-x, 88.0f)));
+    const float y = __builtin_amdgcn_fmed3f(-x, -200.0f, 88.0f);
+    const float L = 1.44269502162933349609375f;
+    const float Llo = 1.925963033500011079e-8f;
+    const float th = y * L;
+    const float tl = fmaf(y, Llo, fmaf(y, L, -th));
+    const float e = __builtin_amdgcn_exp2f(th);
+    return __builtin_amdgcn_rcpf(1.0f + fmaf(e, tl * 0.693147180559945309f, e));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b)

@@ -72,10 +72,11 @@ struct BwdParams {
 // LDS per token group: cand_slots u64 candidate slots; the LDS group stage
 // adds group_scratch_floats floats.
 constexpr int cand_slots(int lpt) { return 3 * lpt; }
-// Workgroup LDS the forward kernels may use (the 64 KB every gfx9 device
-// gives a workgroup); with the LDS group stage at 64 lanes per token this
-// bounds E + G by 3648 (6144 bytes of candidates plus 16 (E + G + 64)).
-constexpr size_t kFwdLdsBytes = 65536;
+// Workgroup LDS the forward kernels may use: gfx950 gives a workgroup up
+// to 160 KB.  With the LDS group stage at 64 lanes per token that bounds
+// E + G by 9792 (6144 bytes of candidates plus 16 (E + G + 64)), above
+// every shape within the other limits (E <= 4096, G <= 64: 72640 bytes).
+constexpr size_t kFwdLdsBytes = 163840;
 constexpr int group_scratch_floats(int E, int G, int lpt)
 {
     return E + G + lpt;
@@ -302,6 +303,14 @@ constexpr int kNchLpt16[] = {1, 2, 4};
 constexpr int kNchLpt32[] = {1, 2, 4};
 constexpr int kNchLpt64[] = {1, 2, 3, 4, 6, 8, 9, 12, 16};
 constexpr int kNchScalar[] = {1, 2, 4, 8, 16};
+
+// Group-limited forward for rows of 32-expert groups (router_grouped.h):
+// 16- or 32-lane tokens of 1, 2 or 4 chunks (E = nch * 4 * lpt), top lists
+// of Q = 2 or 4; false when not built for (lpt, nch, Q).
+bool fwd_grouped16(int lpt, int nch, int dtype, int score, int Q, bool bias,
+                   const FwdParams &p, const Launch &l, hipError_t *err);
+bool fwd_grouped32(int lpt, int nch, int dtype, int score, int Q, bool bias,
+                   const FwdParams &p, const Launch &l, hipError_t *err);
 
 // Each translation unit of kernels defines one pair; they return false when
 // the (LPT, NCH, vec) configuration is not built there.

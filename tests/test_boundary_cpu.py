@@ -189,23 +189,21 @@ def test_loss_geometry_covers_every_element(tmp_path):
 
 
 def test_group_limits_decided_on_the_host():
-    """More than ROUTER_MAX_GROUPS groups, and grouped rows whose LDS group
-    stage would not fit (E + G > ROUTER_GROUP_LDS_MAX_E_PLUS_G), return
-    UNSUPPORTED on the host, without a GPU; shapes at the bound pass every
-    host check and only then need the device (ROUTER_ERR_HIP here)."""
+    """More than ROUTER_MAX_GROUPS groups returns UNSUPPORTED on the host,
+    without a GPU; the largest grouped rows (4096 experts in 64 groups, and
+    rows that take the LDS group stage) pass every host check -- the LDS
+    bound ROUTER_GROUP_LDS_MAX_E_PLUS_G lies above every shape within the
+    other limits -- and only then need the device (ROUTER_ERR_HIP here)."""
     HIP = router.ERR_HIP
     assert fwd(E=130, K=1, G=65, Kg=1, score=1) == UNS
     assert fwd(E=4095, K=1, G=65, Kg=1, score=1) == UNS
-    assert fwd(E=4000, K=2, G=50, Kg=1, score=1) == UNS            # 4050 > 3648
-    assert fwd(E=3648, K=4, G=16, Kg=2, score=1) == UNS            # 3664
+    assert fwd(E=4160, K=2, G=64, Kg=1, score=1) == UNS            # E > 4096
     # the shapes below pass the host checks, so with a usable device they
     # would launch (on the fake addresses): only where there is none
     if router.load().router_device_query(None, None, None, None) == OK:
         return
-    assert fwd(E=3640, K=4, G=8, Kg=2, score=1) == HIP             # 3648: fits
-    assert fwd(E=3584, K=4, G=64, Kg=2, score=1) == HIP            # 3648: fits
-    assert fwd(E=4096, K=8, G=0, Kg=0, score=1) == HIP             # no groups: no bound
-    assert fwd(E=1024, K=8, G=64, Kg=4, score=1) == HIP
+    for E, G in ((4096, 64), (4096, 2), (4090, 2), (4095, 63), (2304, 48), (256, 8)):
+        assert fwd(E=E, K=2 * (E // G >= 2) or 1, G=G, Kg=1, score=1) == HIP, (E, G)
 
 
 def test_aux_loss_workspace_query():

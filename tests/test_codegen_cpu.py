@@ -22,7 +22,11 @@ import pytest
 
 from score_function_top_amd import build
 
-KERNEL_SOURCES = [s for s in build.SOURCES if s.endswith(".hip")]
+# kernel sources as (file, extra flags): the grouped kernels' file is built
+# once per lane width
+KERNEL_SOURCES = [(s, []) if isinstance(s, str) else (s[0], [f"-DROUTER_GROUPED_LPT={s[1]}"])
+                  for s in build.SOURCES
+                  if (s if isinstance(s, str) else s[0]).endswith(".hip")]
 
 
 def join_block_writes(asm):
@@ -75,9 +79,10 @@ def test_detector_flags_a_write_ahead_of_the_restore():
     assert join_block_writes(skip) == []
 
 
-def _asm(src, out_dir):
-    out = os.path.join(out_dir, os.path.splitext(src)[0] + ".s")
-    cmd = ["hipcc", *build.FLAGS, "--cuda-device-only", "-S",
+def _asm(entry, out_dir):
+    src, defs = entry
+    out = os.path.join(out_dir, os.path.splitext(src)[0] + "".join(defs) + ".s")
+    cmd = ["hipcc", *build.FLAGS, *defs, "--cuda-device-only", "-S",
            os.path.join(build.CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -92,6 +97,6 @@ def test_no_vector_writes_ahead_of_exec_restores(tmp_path):
         asms = list(ex.map(lambda s: _asm(s, str(tmp_path)), KERNEL_SOURCES))
     bad = []
     for src, asm in zip(KERNEL_SOURCES, asms):
-        bad += [(src,) + f for f in join_block_writes(asm)]
+        bad += [(src[0],) + f for f in join_block_writes(asm)]
     assert not bad, "vector writes ahead of an exec restore:\n" + "\n".join(
         f"{s}: {k[:80]} {lbl} {ins[:3]}" for s, k, lbl, ins in bad[:20])

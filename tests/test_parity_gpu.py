@@ -194,17 +194,31 @@ def test_groups(T, E, K, G, Kg, dtype, biased):
     run_fwd(wl)
 
 
-@pytest.mark.parametrize("E,G,Kg,K,b", [(3640, 8, 2, 4, 0.05), (3584, 64, 4, 8, 0.0)])
-def test_group_lds_bound(E, G, Kg, K, b):
-    """Grouped rows exactly at the LDS bound of the group stage
-    (E + G = 3648) run and match the oracle; one more expert per group
-    is rejected on the host."""
+@pytest.mark.parametrize("E,G,Kg,K,b", [(4096, 64, 4, 8, 0.05), (4096, 2, 1, 4, 0.0),
+                                        (4092, 62, 8, 16, 0.05)])
+def test_group_largest_rows(E, G, Kg, K, b):
+    """The largest grouped rows (LDS group stage, up to 72 KB of LDS per
+    workgroup) run and match the oracle; more than 64 groups is rejected
+    on the host."""
     wl = edge_wl(70, E, K, synth.SIGMOID, True, bias=b, G=G, Kg=Kg, c=2.5, seed=31)
     run_fwd(wl)
-    x = torch.zeros((4, E + G), device=DEV)
+    x = torch.zeros((4, 130), device=DEV)
     with pytest.raises(router.RouterError) as e:
-        router.router_topk_fwd(x, K, "sigmoid", True, G, Kg)
+        router.router_topk_fwd(x, 2, "sigmoid", True, 65, 1)
     assert e.value.status == router.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("sf,b,dtype,E,G", [(synth.SIGMOID, 0.05, synth.BF16, 256, 8),
+                                            (synth.SOFTMAX, 0.0, synth.F32, 256, 8),
+                                            (synth.SIGMOID, 0.0, synth.F32, 512, 16),
+                                            (synth.SIGMOID, 0.05, synth.F32, 64, 2)])
+def test_grouped_persistent_rows(sf, b, dtype, E, G):
+    """Rows of 32-expert groups on the occupancy-sized grid: with 50001
+    tokens every wave loops over several token groups (the next group's
+    logits in flight) and the last group is ragged."""
+    wl = edge_wl(50001, E, 8, sf, True, bias=b, G=G, Kg=min(4, G), dtype=dtype, c=2.5,
+                 seed=37)
+    run_fwd(wl)
 
 
 def _random_cases(n=48, seed=2024):

@@ -53,7 +53,8 @@ def loss_bytes(kind, T, E, esz):
 KERNEL_SYMBOL = {"topk_fwd": "fwd_kernel", "topk_bwd": "bwd_kernel",
                  "aux_fwd": "fwd_kernel", "aux_bwd": "bwd_kernel",
                  "tokens_per_expert": "count_kernel", "aux_loss_fwd": "loss_kernel",
-                 "aux_loss_bwd": "loss_bwd_kernel"}
+                 "aux_loss_bwd": "loss_bwd_kernel", "shared_gate": "shared_gate_kernel",
+                 "topk_fwd_grouped": "grouped_fwd_kernel"}
 # B300 figures of the fused-router page for this exact shape (context only).
 PAGE_B300_GBPS = {"topk_fwd": 964, "topk_bwd": 2766, "aux_fwd": 891, "aux_bwd": 4201}
 
@@ -68,9 +69,12 @@ _LOSS_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_par
                  "router_loss.hip"]
 _GATE_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",
                  "router_topk_wave.h", "router_gate.hip"]
+_GROUPED_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_kernels.h",
+                    "router_params.h", "router_grouped.h", "router_grouped.hip"]
 SYMBOL_SOURCES = {"fwd_kernel": _ROUTER_SOURCES, "bwd_kernel": _ROUTER_SOURCES,
                   "loss_kernel": _LOSS_SOURCES, "count_kernel": _LOSS_SOURCES,
-                  "loss_bwd_kernel": _LOSS_SOURCES, "shared_gate_kernel": _GATE_SOURCES}
+                  "loss_bwd_kernel": _LOSS_SOURCES, "shared_gate_kernel": _GATE_SOURCES,
+                  "grouped_fwd_kernel": _GROUPED_SOURCES}
 
 
 def path_threshold_desc(router):
@@ -90,43 +94,42 @@ def kernel_source_hash(symbol="fwd_kernel"):
     return h.hexdigest()[:16]
 
 
-def read_traffic(symbol, workload="c4_2304x36"):
-    """Measured HBM bytes per launch of kernel `symbol` from the committed
-    profiler summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{symbol}_{workload}.txt")
+def _summary(path, symbol):
+    """key: value lines of a committed counter summary, or None when it is
+    missing or was taken on other kernel sources than the current ones."""
     if not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
-            vals[k.strip()] = v.strip()
+            vals[k.strip()] = v.split("#")[0].strip()
     if vals.get("kernel_source_hash") != kernel_source_hash(symbol):
         return None
+    return vals
+
+
+def read_traffic(kind, workload="c4_2304x36"):
+    """Measured HBM bytes per launch of pass `kind` from its own committed
+    profiler summary, if that was taken on the current kernel sources."""
+    vals = _summary(os.path.join(ROOT, "profiles", f"hbm_traffic_{kind}_{workload}.txt"),
+                    KERNEL_SYMBOL[kind])
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["hbm_bytes_per_launch"]) if vals else None
     except (KeyError, ValueError):
         return None
 
 
-def read_valu(symbol, workload="c4_2304x36"):
-    """VALU issue of kernel `symbol` from the committed counter summary
+def read_valu(kind, workload="c4_2304x36"):
+    """VALU issue of pass `kind` from its committed counter summary
     (SQ_ACTIVE_INST_VALU in 4-cycle units per launch, and VALU instructions
     per wave), if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"valu_{symbol}_{workload}.txt")
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_source_hash(symbol):
-        return None
+    vals = _summary(os.path.join(ROOT, "profiles", f"valu_{kind}_{workload}.txt"),
+                    KERNEL_SYMBOL[kind])
     try:
         return {"active_valu_quads_per_launch": float(vals["active_valu_quads_per_launch"]),
                 "valu_insts_per_wave": float(vals["valu_insts_per_wave"]),
-                "simds": int(vals["simds"])}
+                "simds": int(vals["simds"])} if vals else None
     except (KeyError, ValueError):
         return None
 
@@ -261,11 +264,20 @@ def cpu_baseline(wl, tokens):
                       f"same byte formula as the GPU value"}
 
 
-def graph_us_per_launch(torch, launches):
+def graph_us_per_launch(torch, launches, replays=1):
     """Captures `launches` (callables that enqueue one kernel each on the
-    current stream) into one HIP graph, replays it, and returns the average
-    microseconds per launch of a timed replay.  Graph replay removes the
-    host-side launch cost, which dominates kernels of a few microseconds."""
+    current stream) into one HIP graph, replays it twice untimed, then
+    `replays` times with one event pair around each replay, and returns the
+    median over replays of the microseconds per launch.  Graph replay
+    removes the host-side launch cost, which dominates kernels of a few
+    microseconds."""
+    return graph_us_stats(torch, launches, replays)["median"]
+
+
+def graph_us_stats(torch, launches, replays=11):
+    """As graph_us_per_launch; returns {"median", "p10", "p90", "replays",
+    "launches"}: per-launch microseconds over the timed replays."""
+    import numpy as np
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -279,21 +291,44 @@ def graph_us_per_launch(torch, launches):
             f()
     for _ in range(2):
         g.replay()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(replays)]
     torch.cuda.synchronize()
-    a.record()
-    g.replay()
-    b.record()
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / len(launches)
+    us = np.array([a.elapsed_time(b) * 1e3 / len(launches) for a, b in evs])
     del g
-    return us
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"median": float(p50), "p10": float(p10), "p90": float(p90), "replays": replays,
+            "launches": len(launches)}
 
 
-def run_sweep(torch, router, synth, np, steps):
-    """Per-pass effective GB/s over the T=8192 E/K grid of the router page's
-    benchmark tables (softmax without renorm, sigmoid with renorm), cold
-    caches (>= 2 GiB of rotating buffer sets per cell)."""
+# Launches per graph for the sweep and config cells: at least this many,
+# cycling through every rotating buffer set.
+CELL_LAUNCHES = 200
+CELL_REPLAYS = 11
+
+
+def cell_launches(f, sets):
+    """max(CELL_LAUNCHES, len(sets)) launches of f cycling through the sets."""
+    n = len(sets)
+    return [lambda st=sets[i % n]: f(st) for i in range(max(CELL_LAUNCHES, n))]
+
+
+def cell_result(nbytes, st):
+    """us (median) and GB/s of a cell, with the spread over replays."""
+    return {"us": round(st["median"], 2), "GBps": round(nbytes / st["median"] / 1e3, 1),
+            "us_p10": round(st["p10"], 2), "us_p90": round(st["p90"], 2)}
+
+
+def run_sweep(torch, router, synth, np):
+    """Per-pass microseconds and effective GB/s over the T=8192 E/K grid of
+    the router page's benchmark tables (softmax without renorm, sigmoid with
+    renorm), cold caches (>= 2 GiB of rotating buffer sets per cell, every
+    set used in each graph of launches)."""
     dev = torch.device("cuda:0")
     out = {}
     for sf in (synth.SOFTMAX, synth.SIGMOID):
@@ -329,15 +364,14 @@ def run_sweep(torch, router, synth, np, steps):
                         for st in sets:
                             calls[kind.replace("bwd", "fwd")](st)
                     f = calls[kind]
-                    us = graph_us_per_launch(
-                        torch, [lambda st=sets[i % n]: f(st) for i in range(steps)])
-                    cell[kind] = round(T * E * BYTES_PER_ELEM[kind] / us / 1e3, 1)
+                    st = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
+                    cell[kind] = cell_result(T * E * BYTES_PER_ELEM[kind], st)
                 out[f"{sname}_{E}x{K}"] = cell
                 del sets, x, g
     return out
 
 
-def run_configs(torch, router, synth, np, steps):
+def run_configs(torch, router, synth, np):
     """Per-pass microseconds and effective GB/s of the five router workloads
     (bias, group-limited and bf16 variants included), cold caches, launches
     replayed from a HIP graph."""
@@ -383,9 +417,9 @@ def run_configs(torch, router, synth, np, steps):
                 for st in sets:
                     calls[kind.replace("bwd", "fwd")](st)
             f = calls[kind]
-            us = graph_us_per_launch(torch, [lambda st=sets[i % n]: f(st) for i in range(steps)])
+            st = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
             nb = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None) else 0)
-            cell[kind] = {"us": round(us, 2), "GBps": round(nb / us / 1e3, 1)}
+            cell[kind] = cell_result(nb, st)
         out[name] = cell
         del sets, x, g
     return out
@@ -404,7 +438,7 @@ def shared_gate_bytes(M, E=512, H=4096, K=10, S=1, esz=2):
     return M * E * esz + M * H * esz + S * H * esz + M * (K + S) * 8
 
 
-def run_shared_gate(torch, router, synth, steps, only_m=None):
+def run_shared_gate(torch, router, synth, only_m=None):
     """Routed top-k with the shared-expert gate at the aiter page's shape
     (E=512 experts, hidden 4096, top-10, one shared expert, bf16) over its
     token sweep; calls replayed from a HIP graph; from M=1024 on the inputs
@@ -424,11 +458,13 @@ def run_shared_gate(torch, router, synth, steps, only_m=None):
         sets = [(x0.clone(), h0.clone()) for _ in range(n)] if n > 1 else [(x0, h0)]
         w = torch.empty((M, K + S), dtype=torch.float32, device=dev)
         ids = torch.empty((M, K + S), dtype=torch.int32, device=dev)
-        calls = [lambda st=sets[i % len(sets)]: router.router_topk_shared_gate(
-            st[0], st[1], g, K, True, 1.0, E, out=(w, ids)) for i in range(steps)]
-        us = graph_us_per_launch(torch, calls)
+        f = lambda st: router.router_topk_shared_gate(st[0], st[1], g, K, True, 1.0, E,
+                                                      out=(w, ids))
+        stt = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
+        us = stt["median"]
         nb = shared_gate_bytes(M, E, H, K, S)
-        out[f"M{M}"] = {"us_graph": round(us, 2), "GBps": round(nb / us / 1e3, 1),
+        out[f"M{M}"] = {"us_graph": round(us, 2), "us_p10": round(stt["p10"], 2),
+                        "us_p90": round(stt["p90"], 2), "GBps": round(nb / us / 1e3, 1),
                         "frac_of_peak": round(nb / us / 1e3 / PEAK_GBPS, 4),
                         "algo_bytes": nb, "cold": n > 1,
                         "page_aiter_fused_us_context": PAGE_AITER_FUSED_US.get(M)}
@@ -458,11 +494,41 @@ def copy_calibration(torch, dev, mib):
             "GBps": round(2 * n / us / 1e3, 1)}
 
 
+# Read:write bytes per element of each pass (fp32), for the same-mix ceiling.
+STREAM_MIX = {"topk_fwd": (4, 9), "topk_bwd": (9, 4), "aux_fwd": (4, 9), "aux_bwd": (8, 4),
+              "copy": (4, 4), "read_only": (4, 0), "write_only": (0, 4)}
+
+
+def run_stream_ceiling(torch, router, T, E):
+    """The bandwidth this device reaches for each pass's read:write mix with
+    no arithmetic: the library's streaming kernel moving the pass's bytes
+    (T*E elements), cold (rotating buffers of >= 2 GiB), timed like the
+    config cells.  GB/s and the share of the 8 TB/s peak."""
+    dev = torch.device("cuda:0")
+    out = {}
+    for kind, (r, w) in STREAM_MIX.items():
+        rb, wb = T * E * r, T * E * w
+        n = max(4, -(-(2 << 30) // (rb + wb)))
+        sets = [(torch.empty(max(rb, 16), dtype=torch.uint8, device=dev),
+                 torch.empty(max(wb, 16), dtype=torch.uint8, device=dev)) for _ in range(n)]
+        for a, _ in sets:
+            a.fill_(1)
+        f = lambda st: router.stream_bandwidth(st[0], rb, st[1], wb)
+        st = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
+        res = cell_result(rb + wb, st)
+        res["frac_of_peak"] = round((rb + wb) / st["median"] / 1e3 / PEAK_GBPS, 4)
+        res["read_write_bytes_per_element"] = [r, w]
+        out[kind] = res
+        del sets
+    return out
+
+
 def run_decode_route(torch, router, synth, steps):
     """Latency of decode-shape routing with expert maps (one workgroup per
     call) at the onnxruntime page's shapes: T in 1..4 rows, E = 512 experts,
     K in {1, 2, 4, 6, 8, 10}, softmax with renormalisation, fp32 logits.
-    us_graph: per call inside a replayed HIP graph of `steps` calls; us_eager:
+    us_graph: per call, median over replays of a HIP graph of CELL_LAUNCHES
+    calls (p10/p90 beside it); us_eager:
     `steps` back-to-back calls on the stream, one event pair (host launch
     included when it is the bottleneck).  floor_us_graph: a one-element fill
     kernel the same way, the cost of any dependent kernel on this device."""
@@ -474,7 +540,8 @@ def run_decode_route(torch, router, synth, steps):
                                                synth.F32)[0]).to(dev)
             res = router.router_route_maps(x, K, "softmax", True)
             f = lambda: router.router_route_maps(x, K, "softmax", True, out=res)
-            g_us = graph_us_per_launch(torch, [f] * steps)
+            gst = graph_us_stats(torch, [f] * CELL_LAUNCHES, CELL_REPLAYS)
+            g_us = gst["median"]
             for _ in range(3):
                 f()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -484,10 +551,12 @@ def run_decode_route(torch, router, synth, steps):
                 f()
             b.record()
             torch.cuda.synchronize()
-            out[f"T{T}_K{K}"] = {"us_graph": round(g_us, 2),
+            out[f"T{T}_K{K}"] = {"us_graph": round(g_us, 2), "us_graph_p10": round(gst["p10"], 2),
+                                 "us_graph_p90": round(gst["p90"], 2),
                                  "us_eager": round(a.elapsed_time(b) * 1e3 / steps, 2)}
     one = torch.zeros(1, device=dev)
-    out["floor_us_graph"] = round(graph_us_per_launch(torch, [one.zero_] * steps), 2)
+    out["floor_us_graph"] = round(graph_us_per_launch(torch, [one.zero_] * CELL_LAUNCHES,
+                                                      CELL_REPLAYS), 2)
     return out
 
 
@@ -532,7 +601,7 @@ def main():
         return
     if args.only_shared_gate:
         torch.cuda.set_device(0)
-        res = {"shared_gate": run_shared_gate(torch, router, synth, args.steps,
+        res = {"shared_gate": run_shared_gate(torch, router, synth,
                                               args.shared_gate_tokens or None),
                "kernel_source_hash": {"gate": kernel_source_hash("shared_gate_kernel")}}
         copy = copy_calibration(torch, torch.device("cuda:0"), args.copy_calibration_mib)
@@ -718,22 +787,26 @@ def main():
     dom = max(by_sym, key=lambda sym: sum(kern[k]["us_avg"] for k in by_sym[sym]))
     us = sum(kern[k]["us_avg"] for k in by_sym[dom]) / len(by_sym[dom])
     nb = sum(kern[k]["algo_bytes"] for k in by_sym[dom]) / len(by_sym[dom])
-    traffic = read_traffic(dom) if args.workload == "c4_softmax_2304x36" and not args.warm else None
+    # the symbol's traffic: the mean over its passes' own counter summaries
+    # (all of them present and current), else null
+    traffic = None
+    if args.workload == "c4_softmax_2304x36" and not args.warm:
+        tr = [read_traffic(k) for k in by_sym[dom]]
+        traffic = round(sum(tr) / len(tr)) if all(t is not None for t in tr) else None
     env = environment(torch, router)
     roof = {"bound": "hbm", "kernel": dom, "passes": by_sym[dom], "us_avg": round(us, 2),
             "achieved": round(nb / us / 1e3, 1), "peak": PEAK_GBPS, "unit": "GB/s",
             "frac": round(nb / us / 1e3 / PEAK_GBPS, 4),
             "algo_bytes_per_launch": int(nb), "traffic": traffic}
     if args.workload == "c4_softmax_2304x36" and not args.warm:
-        roof["valu"] = valu_busy(read_valu(dom), us, env.get("clock_khz"))
+        roof["valu"] = valu_busy(read_valu(by_sym[dom][0]), us, env.get("clock_khz"))
         # the committed counter summaries of every pass's kernel, where they
         # match the current sources
         for kind in kinds:
             if kind in LOSS_KINDS:
                 continue
-            sym = KERNEL_SYMBOL[kind]
-            kern[kind]["traffic"] = read_traffic(sym)
-            kern[kind]["valu"] = valu_busy(read_valu(sym), kern[kind]["us_avg"],
+            kern[kind]["traffic"] = read_traffic(kind)
+            kern[kind]["valu"] = valu_busy(read_valu(kind), kern[kind]["us_avg"],
                                            env.get("clock_khz"))
 
     copy = copy_calibration(torch, dev, args.copy_calibration_mib)
@@ -762,7 +835,8 @@ def main():
         "environment": env,
         "kernel_source_hash": {"router": kernel_source_hash("fwd_kernel"),
                                "loss": kernel_source_hash("loss_kernel"),
-                               "gate": kernel_source_hash("shared_gate_kernel")},
+                               "gate": kernel_source_hash("shared_gate_kernel"),
+                               "grouped": kernel_source_hash("grouped_fwd_kernel")},
     }
     if not args.only:
         loss = {}
@@ -780,7 +854,7 @@ def main():
                           "algo_bytes": nb, "GBps": round(nb / avg / 1e3, 1),
                           "GBps_graph": round(nb / g_us / 1e3, 1),
                           "frac_of_peak": round(nb / avg / 1e3 / PEAK_GBPS, 4),
-                          "traffic": read_traffic(sym) if not args.warm else None}
+                          "traffic": read_traffic(kind) if not args.warm else None}
         out["aux_loss"] = loss
         out["aux_loss_note"] = (
             "load-balancing loss passes on the same workload (not part of the step): "
@@ -799,22 +873,32 @@ def main():
         out["decode_route_note"] = (
             "decode-shape routing with expert maps (one workgroup): microseconds per call, "
             "T rows x E=512 experts x K, softmax renormalised, fp32")
-        out["shared_gate"] = run_shared_gate(torch, router, synth, max(10, args.steps // 4))
+        out["shared_gate"] = run_shared_gate(torch, router, synth)
         m16 = out["shared_gate"]["M16384"]
-        m16["traffic"] = (read_traffic("shared_gate_kernel", "e512_h4096_m16384")
+        m16["traffic"] = (read_traffic("shared_gate", "e512_h4096_m16384")
                           if not args.warm else None)
         out["shared_gate_note"] = (
             "routed softmax top-k with the shared-expert sigmoid gate: M tokens x E=512 x "
             "hidden 4096, top-10, one shared expert, bf16, renormalised; graph-replayed; "
             "GB/s = gating + hidden + gate rows read, weights and ids written")
+    if not args.only and args.workload == "c4_softmax_2304x36":
+        out["stream_ceiling"] = run_stream_ceiling(torch, router, T, E)
+        out["stream_ceiling_note"] = (
+            "the library's streaming kernel (16-byte non-temporal buffer loads and stores, no "
+            "arithmetic) moving each pass's bytes at its read:write mix over T*E elements, "
+            "cold; the bandwidth a kernel with that mix can reach on this device")
     if not args.no_sweep and not args.only:
-        out["configs"] = run_configs(torch, router, synth, np, max(10, args.steps // 4))
-        out["configs_note"] = ("the five router workloads (c1..c5), cold, launches replayed "
-                               "from a HIP graph")
+        out["configs"] = run_configs(torch, router, synth, np)
+        out["configs_note"] = (f"the five router workloads (c1..c5), cold: per pass a HIP graph "
+                               f"of max({CELL_LAUNCHES}, sets) launches cycling through every "
+                               f"rotating buffer set, replayed {CELL_REPLAYS} times; us = median "
+                               f"per launch over the replays, p10/p90 beside it")
         t0 = time.perf_counter()
-        out["sweep_GBps"] = run_sweep(torch, router, synth, np, max(10, args.steps // 4))
-        out["sweep_note"] = (f"T=8192, per-pass effective GB/s, cold (rotating sets), launches "
-                             f"replayed from a HIP graph; softmax without renorm, sigmoid "
+        out["sweep"] = run_sweep(torch, router, synth, np)
+        out["sweep_note"] = (f"T=8192, per pass: us (median per launch over {CELL_REPLAYS} "
+                             f"replays of a HIP graph of max({CELL_LAUNCHES}, sets) launches "
+                             f"cycling through every rotating buffer set, >= 2 GiB: cold), "
+                             f"p10/p90, GB/s from the median; softmax without renorm, sigmoid "
                              f"with renorm; {time.perf_counter() - t0:.1f} s")
     print(json.dumps(out), flush=True)
 

@@ -104,19 +104,21 @@ typedef enum { ROUTER_SOFTMAX = 0, ROUTER_SIGMOID = 1 } router_score_fn;
  * Not implemented (UNSUPPORTED), all decided on the host before any
  * launch: E > ROUTER_MAX_EXPERTS; expert_bias with the softmax;
  * num_groups > ROUTER_MAX_GROUPS (one lane of a 64-lane token scores each
- * group); and, with num_groups > 0, E + num_groups >
- * ROUTER_GROUP_LDS_MAX_E_PLUS_G: where the group stage keeps a copy of the
- * row in LDS (groups that are not 4*2^k experts, K / group_topk > 4, rows
- * of more than 1024 experts, unaligned arrays, or
- * router_set_group_stage(ROUTER_GROUP_STAGE_LDS)) the copy and the
- * candidate lists must fit the 64 KB of LDS a workgroup gets, and they do
- * exactly when E + num_groups <= 3648.  (A device with less LDS per
- * workgroup than 64 KB would also return UNSUPPORTED, after the device
- * query.)  The bound follows the fused-router page, "Hardening" (host-side
- * checks, and the device's shared-memory limit in the buffer decision).
+ * group); with num_groups > 0, E + num_groups >
+ * ROUTER_GROUP_LDS_MAX_E_PLUS_G, where the group stage's LDS copy of the
+ * row (used for groups that are not 4*2^k experts, K / group_topk > 4,
+ * rows of more than 1024 experts, unaligned arrays, or
+ * router_set_group_stage(ROUTER_GROUP_STAGE_LDS)) and the candidate lists
+ * would exceed the 160 KB of LDS a gfx950 workgroup gets -- a bound above
+ * ROUTER_MAX_EXPERTS + ROUTER_MAX_GROUPS, so every grouped shape within
+ * the other limits is supported.  On a device that gives a workgroup less
+ * LDS (not a target of this library), the device query decides, after the
+ * host checks.  The bounds follow the fused-router page, "Hardening"
+ * (host-side checks, and the device's shared-memory limit in the
+ * buffer decision).
  */
 #define ROUTER_MAX_GROUPS 64
-#define ROUTER_GROUP_LDS_MAX_E_PLUS_G 3648
+#define ROUTER_GROUP_LDS_MAX_E_PLUS_G 9792
 router_status router_topk_fwd(const void *logits, int dtype, int64_t T,
                               int32_t E, int32_t K, int score_fn, int renorm,
                               int32_t num_groups, int32_t group_topk,
@@ -383,6 +385,19 @@ router_status router_set_topk_path_threshold(int threshold);
  */
 router_status router_device_query(int32_t *compute_units, int32_t *clock_khz,
                                   int32_t *memory_clock_khz, int32_t *memory_bus_bits);
+
+/*
+ * Bandwidth reference for the measurement (no passage: bookkeeping of the
+ * measurement, like router_device_query).  Reads read_bytes from src and
+ * writes write_bytes to dst (device pointers, 16-byte aligned, sizes
+ * multiples of 16) with the router kernels' access style and no other
+ * work; timing it at a kernel's read:write mix gives the bandwidth this
+ * device reaches for that mix.  dst receives arbitrary contents.  Errors:
+ * negative or unaligned sizes, null or misaligned pointers INVALID_ARG.
+ */
+router_status router_stream_bandwidth(const void *src, int64_t read_bytes,
+                                      void *dst, int64_t write_bytes,
+                                      void *hip_stream);
 
 /*
  * Group stage of the group-limited forward.  Passage: the fused-router

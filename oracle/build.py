@@ -12,8 +12,10 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(src=SRC, out=LIB, extra_flags=()):
-    """Compiles ``src`` into the shared library ``out``; returns ``out``."""
-    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
+    """Compiles ``src`` into the shared library ``out``; returns ``out``.
+    -O3 for the generic x86-64 target: the library is built on one machine
+    and may run on another host CPU, so no -march=native."""
+    cmd = ["gcc", "-O3", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC",
            *extra_flags, src, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)

@@ -22,7 +22,8 @@ ARCH = os.environ.get("ROUTER_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["router_api.cpp", "router_lpt16.hip", "router_lpt32.hip",
            "router_lpt64a.hip", "router_lpt64b.hip", "router_lpt64c.hip",
            "router_scalar.hip", "router_loss.hip", "router_route.hip",
-           "router_gate.hip", ("router_grouped.hip", 16), ("router_grouped.hip", 32)]
+           "router_gate.hip", "router_stream.hip", ("router_grouped.hip", 16),
+           ("router_grouped.hip", 32)]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU forms (v_pk_*_f32) stay off: hipcc otherwise

@@ -312,6 +312,10 @@ bool fwd_grouped16(int lpt, int nch, int dtype, int score, int Q, bool bias,
 bool fwd_grouped32(int lpt, int nch, int dtype, int score, int Q, bool bias,
                    const FwdParams &p, const Launch &l, hipError_t *err);
 
+// Streaming kernel for the bandwidth ceiling (router_stream.hip).
+hipError_t launch_stream(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes,
+                         hipStream_t stream);
+
 // Each translation unit of kernels defines one pair; they return false when
 // the (LPT, NCH, vec) configuration is not built there.
 #define ROUTER_DECLARE_PART(NAME)                                                   \

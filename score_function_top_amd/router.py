@@ -86,6 +86,8 @@ def load():
     lib.router_set_group_stage.restype = ci
     lib.router_get_group_stage.argtypes = []
     lib.router_get_group_stage.restype = ci
+    lib.router_stream_bandwidth.argtypes = [vp, i64, vp, i64, vp]
+    lib.router_stream_bandwidth.restype = ci
     lib.router_status_str.argtypes = [ci]
     lib.router_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -123,6 +125,14 @@ def device_query():
 
 GROUP_STAGE_AUTO = 0
 GROUP_STAGE_LDS = 1
+
+
+def stream_bandwidth(src, read_bytes, dst, write_bytes):
+    """Reads read_bytes of src and writes write_bytes of dst (uint8 GPU
+    tensors) with the router kernels' access style and no other work: the
+    bandwidth reference of a read:write mix (a measurement utility)."""
+    check(load().router_stream_bandwidth(_ptr(src), int(read_bytes), _ptr(dst),
+                                         int(write_bytes), _stream(src)))
 
 
 def set_group_stage(stage):

@@ -371,57 +371,85 @@ def run_sweep(torch, router, synth, np):
     return out
 
 
+def workload_cells(torch, router, synth, np, wl, kinds=None):
+    """Per-pass cells (us median / p10 / p90, GB/s) of one workload, cold:
+    >= 2 GiB of rotating buffer sets, a HIP graph of max(200, sets)
+    launches per pass, replayed CELL_REPLAYS times."""
+    dev = torch.device("cuda:0")
+    T, E, K = wl.T, wl.E, wl.K
+    sname = "softmax" if wl.score_fn == synth.SOFTMAX else "sigmoid"
+    esz = 4 if wl.dtype == synth.F32 else 2
+
+    def host(arr):
+        a = np.ascontiguousarray(arr)
+        if wl.dtype == synth.F32:
+            return torch.from_numpy(a)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+
+    x, g = host(wl.logits()[0]).to(dev), host(wl.grad()[0]).to(dev)
+    bias = wl.bias()
+    bd = None if bias is None else torch.from_numpy(bias).to(dev)
+    set_bytes = T * E * (4 * esz + 4 + 1)
+    n = max(4, -(-(2 << 30) // set_bytes))
+    sets = [{"x": x.clone(), "g": g.clone(), "p": torch.empty_like(x),
+             "dx": torch.empty_like(x),
+             "i": torch.empty(T, E, dtype=torch.float32, device=dev),
+             "m": torch.empty(T, E, dtype=torch.bool, device=dev)} for _ in range(n)]
+    calls = {
+        "topk_fwd": lambda st: router.router_topk_fwd(
+            st["x"], K, sname, wl.renorm, wl.num_groups, wl.group_topk, wl.scaling_factor,
+            bd, out=(st["p"], st["m"], st["i"])),
+        "topk_bwd": lambda st: router.router_topk_bwd(
+            st["g"], st["i"], st["m"], K, sname, wl.renorm, wl.scaling_factor, out=st["dx"]),
+        "aux_fwd": lambda st: router.router_aux_scores(
+            st["x"], K, sname, wl.aux_renorm, out=(st["p"], st["m"], st["i"])),
+        "aux_bwd": lambda st: router.router_aux_scores_bwd(
+            st["g"], st["i"], sname, wl.aux_renorm, out=st["dx"]),
+    }
+    if kinds is None:
+        kinds = ["topk_fwd", "topk_bwd"] + (["aux_fwd", "aux_bwd"] if wl.aux else [])
+    bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
+    cell = {}
+    for kind in kinds:
+        if kind.endswith("bwd"):
+            for st in sets:
+                calls[kind.replace("bwd", "fwd")](st)
+        f = calls[kind]
+        st = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
+        nb = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None) else 0)
+        cell[kind] = cell_result(nb, st)
+    del sets, x, g
+    return cell
+
+
 def run_configs(torch, router, synth, np):
     """Per-pass microseconds and effective GB/s of the five router workloads
     (bias, group-limited and bf16 variants included), cold caches, launches
     replayed from a HIP graph."""
-    dev = torch.device("cuda:0")
+    return {name: workload_cells(torch, router, synth, np, wl)
+            for name, wl in synth.WORKLOADS.items()}
+
+
+GRID_STUDY = ["c2_softmax_256x4", "c4_softmax_2304x36", "c5_group_sigmoid_256x8_bf16"]
+
+
+def run_grid_study(torch, router, synth, np, names=GRID_STUDY):
+    """The top-k forward and backward of each workload under both grid
+    modes of the library: one block per token group ("full", the default)
+    and the occupancy-sized persistent grid ("persistent")."""
     out = {}
-    for name, wl in synth.WORKLOADS.items():
-        T, E, K = wl.T, wl.E, wl.K
-        sname = "softmax" if wl.score_fn == synth.SOFTMAX else "sigmoid"
-        tdt = torch.float32 if wl.dtype == synth.F32 else torch.bfloat16
-        esz = 4 if wl.dtype == synth.F32 else 2
-
-        def host(arr):
-            a = np.ascontiguousarray(arr)
-            if wl.dtype == synth.F32:
-                return torch.from_numpy(a)
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
-
-        x, g = host(wl.logits()[0]).to(dev), host(wl.grad()[0]).to(dev)
-        bias = wl.bias()
-        bd = None if bias is None else torch.from_numpy(bias).to(dev)
-        set_bytes = T * E * (4 * esz + 4 + 1)
-        n = max(4, -(-(2 << 30) // set_bytes))
-        sets = [{"x": x.clone(), "g": g.clone(), "p": torch.empty_like(x),
-                 "dx": torch.empty_like(x),
-                 "i": torch.empty(T, E, dtype=torch.float32, device=dev),
-                 "m": torch.empty(T, E, dtype=torch.bool, device=dev)} for _ in range(n)]
-        calls = {
-            "topk_fwd": lambda st: router.router_topk_fwd(
-                st["x"], K, sname, wl.renorm, wl.num_groups, wl.group_topk, wl.scaling_factor,
-                bd, out=(st["p"], st["m"], st["i"])),
-            "topk_bwd": lambda st: router.router_topk_bwd(
-                st["g"], st["i"], st["m"], K, sname, wl.renorm, wl.scaling_factor, out=st["dx"]),
-            "aux_fwd": lambda st: router.router_aux_scores(
-                st["x"], K, sname, wl.aux_renorm, out=(st["p"], st["m"], st["i"])),
-            "aux_bwd": lambda st: router.router_aux_scores_bwd(
-                st["g"], st["i"], sname, wl.aux_renorm, out=st["dx"]),
-        }
-        kinds = ["topk_fwd", "topk_bwd"] + (["aux_fwd", "aux_bwd"] if wl.aux else [])
-        bpe = BYTES_PER_ELEM if wl.dtype == synth.F32 else BF16_BYTES_PER_ELEM
-        cell = {}
-        for kind in kinds:
-            if kind.endswith("bwd"):
-                for st in sets:
-                    calls[kind.replace("bwd", "fwd")](st)
-            f = calls[kind]
-            st = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
-            nb = T * E * bpe[kind] + (E * 4 if (kind == "topk_fwd" and bias is not None) else 0)
-            cell[kind] = cell_result(nb, st)
-        out[name] = cell
-        del sets, x, g
+    try:
+        for name in names:
+            wl = synth.WORKLOADS[name]
+            res = {}
+            for mode, label in ((router.GRID_FULL, "full"), (router.GRID_PERSISTENT, "persistent")):
+                router.set_grid_mode(mode)
+                for kind, c in workload_cells(torch, router, synth, np, wl,
+                                              ["topk_fwd", "topk_bwd"]).items():
+                    res.setdefault(kind, {})[label] = c
+            out[name] = res
+    finally:
+        router.set_grid_mode(router.GRID_FULL)
     return out
 
 
@@ -579,6 +607,8 @@ def main():
                     help="time only the shared-gate sweep (for profiler runs)")
     ap.add_argument("--shared-gate-tokens", type=int, default=0,
                     help="with --only-shared-gate: one token count instead of the sweep")
+    ap.add_argument("--grid-study", action="store_true",
+                    help="time only the grid study (both grid modes; for profiler runs)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the T=8192 E/K sweep object")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -594,6 +624,10 @@ def main():
     import torch
     from score_function_top_amd import router, synth
 
+    if args.grid_study:
+        torch.cuda.set_device(0)
+        print(json.dumps({"grid_study": run_grid_study(torch, router, synth, np)}), flush=True)
+        return
     if args.only_decode_route:
         torch.cuda.set_device(0)
         print(json.dumps({"decode_route": run_decode_route(torch, router, synth, args.steps)}),
@@ -888,6 +922,11 @@ def main():
             "arithmetic) moving each pass's bytes at its read:write mix over T*E elements, "
             "cold; the bandwidth a kernel with that mix can reach on this device")
     if not args.no_sweep and not args.only:
+        out["grid_study"] = run_grid_study(torch, router, synth, np)
+        out["grid_study_note"] = (
+            "top-k forward and backward under the library's two grid modes: one block per "
+            "token group (full, the default) and the occupancy-sized persistent grid "
+            "(resident blocks per CU x CUs, waves loop over token groups); cells as configs")
         out["configs"] = run_configs(torch, router, synth, np)
         out["configs_note"] = (f"the five router workloads (c1..c5), cold: per pass a HIP graph "
                                f"of max({CELL_LAUNCHES}, sets) launches cycling through every "

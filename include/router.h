@@ -416,6 +416,26 @@ router_status router_stream_bandwidth(const void *src, int64_t read_bytes,
 int router_get_group_stage(void);
 router_status router_set_group_stage(int stage);
 
+/*
+ * Grid of the router's token kernels (forward, backward, aux scores, the
+ * grouped forward).  Passage: the fused-router page, "Forward kernels"
+ * (an occupancy-aware persistent grid, compute_persistent_grid).
+ * ROUTER_GRID_FULL (the default) launches one block per group of tokens a
+ * block holds; ROUTER_GRID_PERSISTENT launches at most the blocks the
+ * device keeps resident for that kernel (its occupancy, from
+ * hipOccupancyMaxActiveBlocksPerMultiprocessor, times the compute units,
+ * read once per device and kernel), and each wave loops over further
+ * token groups (the grouped forward requests the next group's logits
+ * before working on the current one).  The default is the faster on
+ * MI355X for the shapes measured (see the benchmark's grid study); the
+ * results are the same bit for bit.  A process-wide setting; other values
+ * return ROUTER_ERR_INVALID_ARG.
+ */
+#define ROUTER_GRID_FULL 0
+#define ROUTER_GRID_PERSISTENT 1
+int router_get_grid_mode(void);
+router_status router_set_grid_mode(int mode);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,9 @@ int threshold()
 int auto_threshold(int epl) { return epl <= 4 ? 5 : (epl <= 8 ? 4 : 2); }
 
 std::atomic<int> g_group_stage{ROUTER_GROUP_STAGE_AUTO};
+std::atomic<int> g_grid_mode{ROUTER_GRID_FULL};
+
+bool persistent() { return g_grid_mode.load() == ROUTER_GRID_PERSISTENT; }
 
 // ------------------------------------------------------------ devices
 
@@ -201,18 +204,19 @@ int group_reg_log(const Cfg &c, int E, int G, int q)
 }
 
 // Lanes per token of the kernel for rows of 32-expert groups
-// (router_grouped.h) in the layout c the general path chose, so both group
-// stages share their layout and reduction order: E = 32 * G with G a power
-// of two in [2, 16], q = K / Kg <= 4, a vector layout of 16 or 32 lanes
-// with E = nch * 4 * lanes, and at most one selected expert per lane
-// (K <= lanes); 0 when it does not take the shape.
+// (router_grouped.h): E = 32 * G with G a power of two in [2, 16],
+// q = K / Kg <= 4, a vector layout, and at most one selected expert per
+// lane (K <= lanes); 0 when it does not take the shape.  Rows of up to 256
+// experts take 16 lanes (one, two or four chunks), 512 experts 32 lanes
+// (four chunks).  Measured on MI355X at E=256 in 8 groups, bf16 (full grid,
+// interleaved runs): 16 lanes 8.53 us at T=16384 and 28.65 us at T=65536,
+// 32 lanes 11.0 and 31.7 us (8.99 us at T=16384 on the persistent grid).
 int grouped_lpt(const Cfg &c, int E, int G, int K, int Kg)
 {
-    if (G < 2 || G > 16 || E != 32 * G || (G & (G - 1)) != 0 || K / Kg > 4)
+    if (G < 2 || G > 16 || E != 32 * G || (G & (G - 1)) != 0 || K / Kg > 4 || !c.vec)
         return 0;
-    if (!c.vec || (c.lpt != 16 && c.lpt != 32) || E != c.nch * 4 * c.lpt || K > c.lpt)
-        return 0;
-    return c.lpt;
+    const int lpt = E <= 256 ? 16 : 32;
+    return K <= lpt ? lpt : 0;
 }
 
 hipError_t launch_fwd(const Cfg &c, int dtype, int score, int gm, const FwdParams &p,
@@ -324,9 +328,11 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
             p.q = K / Kg;
             p.P = E / G;
             p.scale = scale;
-            const Launch l{grid_for(T, lg), (size_t)tpb * cand_slots(lg) * sizeof(uint64_t),
-                           (hipStream_t)stream};
-            const int nch = c.nch;
+            // LDS: the candidate lists, and a copy of the expert bias
+            const size_t lds = (size_t)tpb * cand_slots(lg) * sizeof(uint64_t) +
+                               (bias ? (size_t)E * sizeof(float) : 0);
+            const Launch l{grid_for(T, lg), lds, (hipStream_t)stream, persistent()};
+            const int nch = E / (4 * lg);
             const int Q = p.q <= 2 ? 2 : 4;
             hipError_t err = hipErrorInvalidValue;
             if (!fwd_grouped16(lg, nch, dtype, score_fn, Q, bias != nullptr, p, l, &err) &&
@@ -372,7 +378,7 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     p.q = G > 0 ? K / Kg : 0;
     p.P = G > 0 ? E / G : 0;
     p.scale = scale;
-    const Launch l{grid_for(T, c.lpt), smem, (hipStream_t)stream};
+    const Launch l{grid_for(T, c.lpt), smem, (hipStream_t)stream, persistent()};
     return launch_fwd(c, dtype, score_fn, gm, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
@@ -413,7 +419,7 @@ router_status bwd_common(const void *g, const float *s, const uint8_t *m, int dt
     p.K = K;
     p.renorm = renorm ? 1 : 0;
     p.scale = scale;
-    const Launch l{grid_for(T, c.lpt), 0, (hipStream_t)stream};
+    const Launch l{grid_for(T, c.lpt), 0, (hipStream_t)stream, persistent()};
     return launch_bwd(c, dtype, score_fn, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 
@@ -754,6 +760,16 @@ router_status router_stream_bandwidth(const void *src, int64_t read_bytes, void 
     return launch_stream(src, read_bytes, dst, write_bytes, (hipStream_t)hip_stream) == hipSuccess
                ? ROUTER_OK
                : ROUTER_ERR_HIP;
+}
+
+int router_get_grid_mode(void) { return g_grid_mode.load(); }
+
+router_status router_set_grid_mode(int mode)
+{
+    if (mode != ROUTER_GRID_FULL && mode != ROUTER_GRID_PERSISTENT)
+        return ROUTER_ERR_INVALID_ARG;
+    g_grid_mode.store(mode);
+    return ROUTER_OK;
 }
 
 int router_get_group_stage(void) { return g_group_stage.load(); }

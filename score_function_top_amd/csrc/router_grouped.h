@@ -30,6 +30,8 @@
 //    at the K-th position).
 #pragma once
 
+#include <type_traits>
+
 #include "router_kernels.h"
 
 namespace rker {
@@ -37,7 +39,7 @@ namespace rker {
 // Group-limited forward for 32-expert groups.  Q: length of the per-group
 // top lists (q <= Q); BIAS: an expert bias is given.
 template <int LPT, int NCH, typename TIn, int SCORE, int Q, bool BIAS>
-__global__ void __launch_bounds__(kBlock, NCH <= 2 ? 5 : 4) grouped_fwd_kernel(FwdParams p)
+__global__ void __launch_bounds__(kBlock, NCH <= 2 ? 6 : 4) grouped_fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // tokens per wave
     constexpr int TPB = kWaves * GPW;        // tokens per block
@@ -57,30 +59,55 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 5 : 4) grouped_fwd_kernel(F
     const uint32_t goff = (uint32_t)(grp * E);
     const int seg = lane >> 3;               // group slot within a chunk
 
-    // the expert bias, shared by every token (default cache policy): once
-    // per wave
-    [[maybe_unused]] float b[NCH][4];
+    // The expert bias, shared by every token: copied once per block into
+    // LDS after the candidate lists and read per token group (no registers
+    // held across the loop).
+    [[maybe_unused]] const float *bl = reinterpret_cast<const float *>(smem + TPB * cand_slots(LPT));
     if constexpr (BIAS) {
-        const rsrc_t rb = make_rsrc(p.bias, (uint32_t)E * 4u);
-#pragma unroll
-        for (int c = 0; c < NCH; c++)
-            load_chunk<LPT, float, true, 0>(rb, 0u, c, j_lane, E, 0.0f, b[c]);
+        float *bw = reinterpret_cast<float *>(smem + TPB * cand_slots(LPT));
+        for (int j = (int)threadIdx.x; j < E; j += kBlock)
+            bw[j] = p.bias[j];
+        __syncthreads();
     }
 
-    // Logits of token group tb (this wave's tokens of the block's group).
-    // Rows have no padding (E == NCH*4*LPT): a masked load (a token past T)
-    // reads 0, and that token's outputs are dropped.
-    auto load_x = [&](int64_t tb_, float (&dst)[NCH][4]) {
+    // Logits of token group tb (this wave's tokens of the block's group), as
+    // loaded: RAW words per chunk (bf16: two 32-bit words of two values
+    // each; fp32: four values).  Rows have no padding (E == NCH*4*LPT): a
+    // masked load (a token past T) reads 0, and that token's outputs are
+    // dropped.
+    constexpr bool BF = sizeof(TIn) == 2;
+    using raw_t = std::conditional_t<BF, uint32_t __attribute__((ext_vector_type(2))),
+                                     uint32_t __attribute__((ext_vector_type(4)))>;
+    auto load_x = [&](int64_t tb_, raw_t (&dst)[NCH]) {
         const int64_t t0_ = tb_ + wave * GPW;
         const int64_t left_ = p.T - t0_;
         const int nval_ = left_ <= 0 ? 0 : (left_ >= GPW ? GPW : (int)left_);
         const int64_t off_ = nval_ ? t0_ * (int64_t)E : 0;
         const rsrc_t r = make_rsrc(static_cast<const TIn *>(p.x) + off_,
                                    (uint32_t)(nval_ * E) * io<TIn>::kSize);
+        const int off = grp < nval_ ? (int)((goff + (uint32_t)j_lane) * io<TIn>::kSize)
+                                    : (int)kOOB;
 #pragma unroll
-        for (int c = 0; c < NCH; c++)
-            io<TIn>::load4(r, grp < nval_ ? (goff + (uint32_t)j_lane) * io<TIn>::kSize : kOOB,
-                           (uint32_t)jrel<LPT>(c, 0) * io<TIn>::kSize, dst[c]);
+        for (int c = 0; c < NCH; c++) {
+            const int soff = (int)((uint32_t)jrel<LPT>(c, 0) * io<TIn>::kSize);
+            if constexpr (BF)
+                dst[c] = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kStream);
+            else
+                dst[c] = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kStream);
+        }
+    };
+    auto unpack = [](const raw_t &w, float (&v)[4]) {
+        if constexpr (BF) {
+            v[0] = as_f(w[0] << 16);
+            v[1] = as_f(w[0] & 0xFFFF0000u);
+            v[2] = as_f(w[1] << 16);
+            v[3] = as_f(w[1] & 0xFFFF0000u);
+        } else {
+            v[0] = as_f(w[0]);
+            v[1] = as_f(w[1]);
+            v[2] = as_f(w[2]);
+            v[3] = as_f(w[3]);
+        }
     };
 
     // Grid-stride over token groups, the next group's logits requested
@@ -88,7 +115,7 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 5 : 4) grouped_fwd_kernel(F
     // (the host's choice) every wave streams its loads behind its compute.
     const int64_t step = (int64_t)gridDim.x * TPB;
     int64_t tb = (int64_t)blockIdx.x * TPB;
-    float xn[NCH][4];
+    raw_t xn[NCH];
     load_x(tb, xn);
     for (; tb < p.T; tb += step) {
         const int64_t t0 = tb + wave * GPW;
@@ -101,9 +128,7 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 5 : 4) grouped_fwd_kernel(F
         float key[NCH][4];
 #pragma unroll
         for (int c = 0; c < NCH; c++)
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                key[c][u] = xn[c][u];
+            unpack(xn[c], key[c]);
         if (tb + step < p.T)
             load_x(tb + step, xn);
 
@@ -148,10 +173,13 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 5 : 4) grouped_fwd_kernel(F
         };
         if constexpr (BIAS) {
 #pragma unroll
-            for (int c = 0; c < NCH; c++)
+            for (int c = 0; c < NCH; c++) {
+                typedef float f4 __attribute__((ext_vector_type(4)));
+                const f4 b = *reinterpret_cast<const f4 *>(bl + jrel<LPT>(c, 0) + j_lane);
 #pragma unroll
                 for (int u = 0; u < 4; u++)
-                    key[c][u] = s[c][u] + b[c][u];
+                    key[c][u] = s[c][u] + b[u];
+            }
         }
 
         // ---- the intermediate is final: store it now (overlaps the rest)
@@ -232,19 +260,27 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 5 : 4) grouped_fwd_kernel(F
         // selection as 0/1 floats: the map bytes (one conversion per byte),
         // the renormalisation sum and the probs take them without selects
         const float tx = tok ? t.x : INFINITY;
-        const bool ties = wave_any(t.j != 0xFFFFFFFFu);
-        const int jt = (int)t.j - j_lane;
         float mf[NCH][4];
+        if (!wave_any(t.j != 0xFFFFFFFFu)) {
+            // no tie straddles any threshold of the wave: one compare each
 #pragma unroll
-        for (int c = 0; c < NCH; c++)
+            for (int c = 0; c < NCH; c++)
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const float k = key[c][u];
-                const bool in = ties ? (k > tx || (k == tx && (t.j == 0xFFFFFFFFu ||
-                                                              jrel<LPT>(c, u) <= jt)))
-                                     : k >= tx;
-                mf[c][u] = in ? 1.0f : 0.0f;
-            }
+                for (int u = 0; u < 4; u++)
+                    mf[c][u] = key[c][u] >= tx ? 1.0f : 0.0f;
+        } else {
+            // equal keys at the threshold: up to expert j_t (bitwise
+            // operators: no short-circuit branches per element)
+            const int jt = t.j == 0xFFFFFFFFu ? 0x7FFFFFFF : (int)t.j - j_lane;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const float k = key[c][u];
+                    const int in = (int)(k > tx) | ((int)(k == tx) & (int)(jrel<LPT>(c, u) <= jt));
+                    mf[c][u] = in ? 1.0f : 0.0f;
+                }
+        }
         float sm[NCH][4];    // s on the selected experts, +0 elsewhere (s >= 0)
 #pragma unroll
         for (int c = 0; c < NCH; c++)

@@ -3,9 +3,9 @@
 // width (ROUTER_GROUPED_LPT), so the two compile in parallel.
 #include <hip/hip_runtime.h>
 
-#include <mutex>
 #include <type_traits>
 
+#include "router_grid.h"
 #include "router_grouped.h"
 
 #ifndef ROUTER_GROUPED_LPT
@@ -21,37 +21,11 @@ struct tag {
     using type = T;
 };
 
-// Occupancy-sized grid: the kernel's resident blocks per compute unit
-// (hipOccupancyMaxActiveBlocksPerMultiprocessor, read once per device and
-// kernel) times the compute units, or fewer when the tokens need fewer.
-// Each wave then loops over token groups with the next group's logits in
-// flight behind its work.  Measured on MI355X at T=16384, E=256 in 8
-// groups, bf16 (5 resident blocks per CU): 1280 blocks 9.4 us; one block
-// per two-token wave pair (2048 blocks) 12.3 us; 6 per CU 11.3 us, and 2,
-// 3, 4 per CU 14.2, 11.4, 10.5 us.
 template <int LPT, int NCH, typename TIn, int SCORE, int Q, bool BIAS>
 hipError_t grouped_one(const FwdParams &p, const Launch &l)
 {
-    const auto kern = grouped_fwd_kernel<LPT, NCH, TIn, SCORE, Q, BIAS>;
-    constexpr int kMaxDev = 64;
-    static std::once_flag once[kMaxDev];
-    static int blocks_per_device[kMaxDev];
-    int d = 0;
-    hipError_t e = hipGetDevice(&d);
-    if (e != hipSuccess)
-        return e;
-    if (d < 0 || d >= kMaxDev)
-        return hipErrorInvalidDevice;
-    std::call_once(once[d], [&] {
-        int occ = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kBlock, l.smem) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess)
-            occ = cus = 0;
-        blocks_per_device[d] = occ * cus;
-    });
-    const unsigned cap = (unsigned)blocks_per_device[d];
-    const unsigned grid = cap > 0 && l.grid > cap ? cap : l.grid;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), l.smem, l.stream, p);
+    constexpr auto k = grouped_fwd_kernel<LPT, NCH, TIn, SCORE, Q, BIAS>;
+    hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), dim3(kBlock), l.smem, l.stream, p);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 
 #include <type_traits>
 
+#include "router_grid.h"
 #include "router_kernels.h"
 
 namespace rker {
@@ -19,20 +20,21 @@ namespace rker {
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, bool VEC>
 hipError_t fwd_sel(const FwdParams &p, int gm, const Launch &l)
 {
-    dim3 g(l.grid), b(kBlock);
+    const dim3 b(kBlock);
     if (gm == GROUP_LDS) {
-        hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_LDS, VEC>), g, b,
-                           l.smem, l.stream, p);
+        constexpr auto k = fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_LDS, VEC>;
+        hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), b, l.smem, l.stream, p);
     } else if (gm == GROUP_REG) {
         // built for vector kernels of up to kGroupRegMaxNch chunks only
-        if constexpr (VEC && NCH <= kGroupRegMaxNch)
-            hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_REG, VEC>), g, b,
-                               l.smem, l.stream, p);
-        else
+        if constexpr (VEC && NCH <= kGroupRegMaxNch) {
+            constexpr auto k = fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_REG, VEC>;
+            hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), b, l.smem, l.stream, p);
+        } else {
             return hipErrorInvalidValue;
+        }
     } else {
-        hipLaunchKernelGGL((fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_NONE, VEC>), g, b,
-                           l.smem, l.stream, p);
+        constexpr auto k = fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_NONE, VEC>;
+        hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), b, l.smem, l.stream, p);
     }
     return hipGetLastError();
 }
@@ -47,8 +49,8 @@ hipError_t fwd_one(const FwdParams &p, int gm, const Launch &l)
 template <int LPT, int NCH, typename TIn, int SCORE, bool VEC>
 hipError_t bwd_one(const BwdParams &p, const Launch &l)
 {
-    hipLaunchKernelGGL((bwd_kernel<LPT, NCH, TIn, SCORE, VEC>), dim3(l.grid), dim3(kBlock), 0,
-                       l.stream, p);
+    constexpr auto k = bwd_kernel<LPT, NCH, TIn, SCORE, VEC>;
+    hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), dim3(kBlock), 0, l.stream, p);
     return hipGetLastError();
 }
 

@@ -83,9 +83,10 @@ constexpr int group_scratch_floats(int E, int G, int lpt)
 }
 
 struct Launch {
-    unsigned grid;
+    unsigned grid;       // one block per token group
     size_t smem;
     hipStream_t stream;
+    bool persistent;     // cap the grid at the kernel's resident blocks
 };
 
 // Column-stripe geometry of the aux-loss kernels (tokens per expert, the

@@ -86,6 +86,10 @@ def load():
     lib.router_set_group_stage.restype = ci
     lib.router_get_group_stage.argtypes = []
     lib.router_get_group_stage.restype = ci
+    lib.router_set_grid_mode.argtypes = [ci]
+    lib.router_set_grid_mode.restype = ci
+    lib.router_get_grid_mode.argtypes = []
+    lib.router_get_grid_mode.restype = ci
     lib.router_stream_bandwidth.argtypes = [vp, i64, vp, i64, vp]
     lib.router_stream_bandwidth.restype = ci
     lib.router_status_str.argtypes = [ci]
@@ -133,6 +137,18 @@ def stream_bandwidth(src, read_bytes, dst, write_bytes):
     bandwidth reference of a read:write mix (a measurement utility)."""
     check(load().router_stream_bandwidth(_ptr(src), int(read_bytes), _ptr(dst),
                                          int(write_bytes), _stream(src)))
+
+
+GRID_FULL = 0
+GRID_PERSISTENT = 1
+
+
+def set_grid_mode(mode):
+    check(load().router_set_grid_mode(int(mode)))
+
+
+def get_grid_mode():
+    return load().router_get_grid_mode()
 
 
 def set_group_stage(stage):

@@ -188,6 +188,18 @@ def test_loss_geometry_covers_every_element(tmp_path):
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
 
 
+def test_grid_mode_setting():
+    assert router.get_grid_mode() == router.GRID_FULL
+    lib = router.load()
+    assert lib.router_set_grid_mode(2) == INV and lib.router_set_grid_mode(-1) == INV
+    router.set_grid_mode(router.GRID_PERSISTENT)
+    try:
+        assert router.get_grid_mode() == router.GRID_PERSISTENT
+    finally:
+        router.set_grid_mode(router.GRID_FULL)
+    assert router.get_grid_mode() == router.GRID_FULL
+
+
 def test_group_limits_decided_on_the_host():
     """More than ROUTER_MAX_GROUPS groups returns UNSUPPORTED on the host,
     without a GPU; the largest grouped rows (4096 experts in 64 groups, and

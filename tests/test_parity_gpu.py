@@ -357,10 +357,11 @@ def _group_stage_outputs(wl, x_st, stage):
 
 @pytest.mark.parametrize("T,E,K,G,Kg,dtype,sf,b", GROUP_STAGE_CASES)
 def test_group_stage_parity(T, E, K, G, Kg, dtype, sf, b):
-    """The register and the LDS group stages agree bit for bit (same group
-    scores, so the same maps and outputs), on random logits and on integer
-    logits whose groups tie; the register stage matches the oracle on both,
-    exactly on the map where groups tie."""
+    """The register (or 32-expert-group) and the LDS group stages agree: the
+    same group scores, so the same maps and intermediates bit for bit (the
+    probs to the last bits of their renormalisation sums), on random logits
+    and on integer logits whose groups tie; the register stage matches the
+    oracle on both, exactly on the map where groups tie."""
     wl = edge_wl(T, E, K, sf, True, bias=b, G=G, Kg=Kg, dtype=dtype, c=2.5, seed=29)
     run_fwd(wl)
 
@@ -376,8 +377,16 @@ def test_group_stage_parity(T, E, K, G, Kg, dtype, sf, b):
         say(f"[group stage] {wl.name} {name}")
         reg = _group_stage_outputs(wl, xs, router.GROUP_STAGE_AUTO)
         lds = _group_stage_outputs(wl, xs, router.GROUP_STAGE_LDS)
-        for u, v in zip(reg, lds):
-            assert torch.equal(u, v), f"{wl.name} {name}: group stages differ"
+        # same group scores: the same maps and intermediates bit for bit; the
+        # probs' renormalisation sums may take another lane layout (rows of
+        # 32-expert groups have their own kernel), so their last bits may differ
+        assert torch.equal(reg[1], lds[1]), f"{wl.name} {name}: maps differ"
+        assert torch.equal(reg[2], lds[2]), f"{wl.name} {name}: intermediates differ"
+        if dtype == synth.F32:
+            assert_close(f64(reg[0]), f64(lds[0]), dtype, f"{wl.name} {name} probs",
+                         rtol=1e-6, atol=0)
+        else:
+            assert_close(f64(reg[0]), f64(lds[0]), dtype, f"{wl.name} {name} probs")
 
     # Logits in {0, 1, 2} and no bias: groups tie exactly when their top-q
     # multisets are equal (the lower group wins), and otherwise differ by far
@@ -481,6 +490,42 @@ def test_path_parity(T, E, K, sf, b, G):
         assert (o[1] == outs[0][1]).all(), "maps differ between paths"
         assert_close(o[0], outs[0][0], synth.F32, "probs across paths", rtol=1e-6, atol=0)
         assert_close(o[2], outs[0][2], synth.F32, "intermediate across paths", rtol=1e-6, atol=0)
+
+
+GRID_CASES = [("c4_softmax_2304x36", 2048), ("c5_group_sigmoid_256x8_bf16", None),
+              ("c2_softmax_256x4", None), ("c3_sigmoid_512x22", 4097)]
+
+
+@pytest.mark.parametrize("name,T", GRID_CASES)
+def test_grid_modes_identical(name, T):
+    """The occupancy-sized persistent grid (waves loop over token groups;
+    the grouped forward prefetches the next group) gives the same bits as
+    one block per token group: forward, backward, aux scores."""
+    wl = WL[name]
+    x_st, _ = wl.logits()
+    g_st, _ = wl.grad()
+    if T is not None:
+        x_st, g_st = x_st[:T], g_st[:T]
+    bias = wl.bias()
+    bt = None if bias is None else torch.from_numpy(bias).to(DEV)
+    xt, gt = to_dev(x_st, wl.dtype), to_dev(g_st, wl.dtype)
+    sf = SCORE_NAME[wl.score_fn]
+    outs = []
+    try:
+        for mode in (router.GRID_FULL, router.GRID_PERSISTENT):
+            say(f"[grid] {name} mode {mode}")
+            router.set_grid_mode(mode)
+            p, m, i = router.router_topk_fwd(xt, wl.K, sf, wl.renorm, wl.num_groups,
+                                             wl.group_topk, wl.scaling_factor, bt)
+            dx = router.router_topk_bwd(gt, i, m, wl.K, sf, wl.renorm, wl.scaling_factor)
+            a = router.router_aux_scores(xt, wl.K, sf, wl.aux_renorm)
+            adx = router.router_aux_scores_bwd(gt, a[2], sf, wl.aux_renorm)
+            torch.cuda.synchronize()
+            outs.append((p, m, i, dx, *a, adx))
+    finally:
+        router.set_grid_mode(router.GRID_FULL)
+    for u, v in zip(*outs):
+        assert torch.equal(u, v), f"{name}: grid modes differ"
 
 
 def test_deterministic():

@@ -588,6 +588,19 @@ def run_decode_route(torch, router, synth, steps):
     return out
 
 
+def workload_by_name(synth, name):
+    """One of the five workloads, or a sweep cell named
+    sweep_<softmax|sigmoid>_<E>x<K> (T=8192)."""
+    if name in synth.WORKLOADS:
+        return synth.WORKLOADS[name]
+    parts = name.split("_")
+    if len(parts) == 3 and parts[0] == "sweep" and parts[1] in ("softmax", "sigmoid"):
+        E, K = (int(v) for v in parts[2].split("x"))
+        return synth.sweep_workload(E, K, synth.SOFTMAX if parts[1] == "softmax"
+                                    else synth.SIGMOID)
+    raise SystemExit(f"bench.py: unknown workload {name}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -607,6 +620,8 @@ def main():
                     help="time only the shared-gate sweep (for profiler runs)")
     ap.add_argument("--shared-gate-tokens", type=int, default=0,
                     help="with --only-shared-gate: one token count instead of the sweep")
+    ap.add_argument("--grid-mode", choices=["full", "persistent"], default="full",
+                    help="the library's grid mode for the whole run (for profiler runs)")
     ap.add_argument("--grid-study", action="store_true",
                     help="time only the grid study (both grid modes; for profiler runs)")
     ap.add_argument("--no-sweep", action="store_true",
@@ -644,7 +659,9 @@ def main():
         print(json.dumps(res), flush=True)
         return
 
-    wl = synth.WORKLOADS[args.workload]
+    router.set_grid_mode(router.GRID_PERSISTENT if args.grid_mode == "persistent"
+                         else router.GRID_FULL)
+    wl = workload_by_name(synth, args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T, E, K = wl.T, wl.E, wl.K
@@ -854,8 +871,7 @@ def main():
                          "note": "the same steps captured in one HIP graph and replayed"},
         "dtype": "f32" if wl.dtype == synth.F32 else "bf16",
         "data": "synthetic (seeded numpy PCG64 logits and gradients)",
-        "config": {"workload": f"{wl.name}: fused MoE router, T={T} tokens, E={E} experts, "
-                               f"K={K}, {sname}, step = " + " + ".join(kinds),
+        "config": {"workload": f"{wl.name} ({' + '.join(kinds)})",
                    "T": T, "E": E, "K": K, "score_function": sname,
                    "logits": f"N(0, std {wl.logit_std})", "renorm": wl.renorm,
                    "cache": "warm (one buffer set)" if args.warm else
@@ -916,11 +932,13 @@ def main():
             "hidden 4096, top-10, one shared expert, bf16, renormalised; graph-replayed; "
             "GB/s = gating + hidden + gate rows read, weights and ids written")
     if not args.only and args.workload == "c4_softmax_2304x36":
-        out["stream_ceiling"] = run_stream_ceiling(torch, router, T, E)
+        out["stream_ceiling"] = {f"T{T}_E{E}": run_stream_ceiling(torch, router, T, E),
+                                 "T8192_E256": run_stream_ceiling(torch, router, 8192, 256)}
         out["stream_ceiling_note"] = (
             "the library's streaming kernel (16-byte non-temporal buffer loads and stores, no "
             "arithmetic) moving each pass's bytes at its read:write mix over T*E elements, "
-            "cold; the bandwidth a kernel with that mix can reach on this device")
+            "cold; the bandwidth a kernel with that mix can reach on this device, at the "
+            "headline size and at the E=256 sweep cells' size")
     if not args.no_sweep and not args.only:
         out["grid_study"] = run_grid_study(torch, router, synth, np)
         out["grid_study_note"] = (

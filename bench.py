@@ -548,6 +548,24 @@ def run_stream_ceiling(torch, router, T, E):
         res["read_write_bytes_per_element"] = [r, w]
         out[kind] = res
         del sets
+    if E % 256 == 0 and E <= 4096:
+        # the forward's own pattern: one wave per row, the row read whole,
+        # then two fp32 rows and one byte row written
+        nb = T * E * 13
+        n = max(4, -(-(2 << 30) // nb))
+        sets = [(torch.empty(T, E, dtype=torch.float32, device=dev),
+                 torch.empty(T, E, dtype=torch.float32, device=dev),
+                 torch.empty(T, E, dtype=torch.float32, device=dev),
+                 torch.empty(T, E, dtype=torch.uint8, device=dev)) for _ in range(n)]
+        for st in sets:
+            st[0].fill_(1.0)
+        f = lambda st: router.row_stream_bandwidth(*st)
+        st = graph_us_stats(torch, cell_launches(f, sets), CELL_REPLAYS)
+        res = cell_result(nb, st)
+        res["frac_of_peak"] = round(nb / st["median"] / 1e3 / PEAK_GBPS, 4)
+        res["read_write_bytes_per_element"] = [4, 9]
+        out["topk_fwd_row_pattern"] = res
+        del sets
     return out
 
 
@@ -938,7 +956,9 @@ def main():
             "the library's streaming kernel (16-byte non-temporal buffer loads and stores, no "
             "arithmetic) moving each pass's bytes at its read:write mix over T*E elements, "
             "cold; the bandwidth a kernel with that mix can reach on this device, at the "
-            "headline size and at the E=256 sweep cells' size")
+            "headline size and at the E=256 sweep cells' size; topk_fwd_row_pattern moves "
+            "the forward's bytes in the forward's own pattern (one wave per row, the row read "
+            "whole, then two fp32 rows and a byte row written), no arithmetic")
     if not args.no_sweep and not args.only:
         out["grid_study"] = run_grid_study(torch, router, synth, np)
         out["grid_study_note"] = (

@@ -400,6 +400,22 @@ router_status router_stream_bandwidth(const void *src, int64_t read_bytes,
                                       void *hip_stream);
 
 /*
+ * Bandwidth reference in the forward's own access pattern (no passage:
+ * bookkeeping of the measurement).  One 64-lane wave per row of E fp32
+ * values (E a multiple of 256, 256..4096): the row is read whole (16 bytes
+ * per lane and chunk), then written to out_a and out_b (E floats per row)
+ * and one byte per element to out_map (the value's sign bit), with no
+ * other work.  x, out_a, out_b: [T, E] fp32, 16-byte aligned; out_map:
+ * [T, E] bytes, 4-byte aligned; device pointers.  Timing it gives the
+ * bandwidth a one-row-per-wave forward reaches at best.  Errors: T < 0, E
+ * out of range or not a multiple of 256, null or misaligned pointers
+ * (T > 0) INVALID_ARG.
+ */
+router_status router_row_stream_bandwidth(const float *x, float *out_a, float *out_b,
+                                          uint8_t *out_map, int64_t T, int64_t E,
+                                          void *hip_stream);
+
+/*
  * Group stage of the group-limited forward.  Passage: the fused-router
  * page, "Hardening" (group-limited routing: topk divisible by group_topk,
  * and the shared-memory limit that decides how a kernel buffers its data).

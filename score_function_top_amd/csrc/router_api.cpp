@@ -762,6 +762,21 @@ router_status router_stream_bandwidth(const void *src, int64_t read_bytes, void 
                : ROUTER_ERR_HIP;
 }
 
+router_status router_row_stream_bandwidth(const float *x, float *out_a, float *out_b,
+                                          uint8_t *out_map, int64_t T, int64_t E,
+                                          void *hip_stream)
+{
+    if (T < 0 || E < 256 || E > 4096 || E % 256 != 0)
+        return ROUTER_ERR_INVALID_ARG;
+    if (T > 0 && (!x || !out_a || !out_b || !out_map || !aligned(x, 16) || !aligned(out_a, 16) ||
+                  !aligned(out_b, 16) || !aligned(out_map, 4)))
+        return ROUTER_ERR_INVALID_ARG;
+    return launch_row_stream(x, out_a, out_b, out_map, T, (int)E, (hipStream_t)hip_stream) ==
+                   hipSuccess
+               ? ROUTER_OK
+               : ROUTER_ERR_HIP;
+}
+
 int router_get_grid_mode(void) { return g_grid_mode.load(); }
 
 router_status router_set_grid_mode(int mode)

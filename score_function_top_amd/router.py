@@ -92,6 +92,8 @@ def load():
     lib.router_get_grid_mode.restype = ci
     lib.router_stream_bandwidth.argtypes = [vp, i64, vp, i64, vp]
     lib.router_stream_bandwidth.restype = ci
+    lib.router_row_stream_bandwidth.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.router_row_stream_bandwidth.restype = ci
     lib.router_status_str.argtypes = [ci]
     lib.router_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -137,6 +139,17 @@ def stream_bandwidth(src, read_bytes, dst, write_bytes):
     bandwidth reference of a read:write mix (a measurement utility)."""
     check(load().router_stream_bandwidth(_ptr(src), int(read_bytes), _ptr(dst),
                                          int(write_bytes), _stream(src)))
+
+
+def row_stream_bandwidth(x, out_a, out_b, out_map):
+    """Moves the forward's bytes in the forward's own pattern (one wave per
+    row of x [T, E] fp32: the row read whole, then written to out_a and
+    out_b, one byte per element to out_map) with no other work: the
+    bandwidth reference of a one-row-per-wave forward (a measurement
+    utility)."""
+    T, E = x.shape
+    check(load().router_row_stream_bandwidth(_ptr(x), _ptr(out_a), _ptr(out_b), _ptr(out_map),
+                                             int(T), int(E), _stream(x)))
 
 
 GRID_FULL = 0

@@ -331,3 +331,21 @@ def test_shared_gate_host_checks():
                    (dict(x=P + 1), INV), (dict(w=P + 2), INV),
                    (dict(M=2 ** 61), OVF), (dict(M=0), OK), (dict(M=0, x=None, w=None), OK)):
         assert call(**kw) == st, kw
+
+
+def test_bandwidth_reference_host_checks():
+    """The two data-movement references reject bad sizes and pointers on
+    the host; T = 0 or empty sizes launch nothing."""
+    lib = router.load()
+    assert lib.router_stream_bandwidth(P, 15, P, 16, None) == INV
+    assert lib.router_stream_bandwidth(P, -16, P, 16, None) == INV
+    assert lib.router_stream_bandwidth(None, 16, P, 16, None) == INV
+    assert lib.router_stream_bandwidth(P + 8, 16, P, 16, None) == INV
+    assert lib.router_stream_bandwidth(None, 0, None, 0, None) == OK
+    row = lib.router_row_stream_bandwidth
+    for T, E in ((8, 255), (8, 300), (8, 4352), (8, 0), (-1, 256)):
+        assert row(P, P, P, P, T, E, None) == INV, (T, E)
+    assert row(None, P, P, P, 8, 256, None) == INV
+    assert row(P, P + 4, P, P, 8, 256, None) == INV
+    assert row(P, P, P, P + 2, 8, 256, None) == INV
+    assert row(None, None, None, None, 0, 2304, None) == OK

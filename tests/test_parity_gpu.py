@@ -492,8 +492,21 @@ def test_path_parity(T, E, K, sf, b, G):
         assert_close(o[2], outs[0][2], synth.F32, "intermediate across paths", rtol=1e-6, atol=0)
 
 
-GRID_CASES = [("c4_softmax_2304x36", 2048), ("c5_group_sigmoid_256x8_bf16", None),
-              ("c2_softmax_256x4", None), ("c3_sigmoid_512x22", 4097)]
+# (workload, token rows): the full C4 batch (4 rows per persistent block),
+# ragged row counts, and 6- and 8-chunk rows (E=1536, E=2048 bf16)
+GRID_CASES = [("c4_softmax_2304x36", None), ("c4_softmax_2304x36", 6001),
+              ("c5_group_sigmoid_256x8_bf16", None),
+              ("c2_softmax_256x4", None), ("c3_sigmoid_512x22", 4097),
+              ("sweep_softmax_1536x8", 5003), ("sweep_sigmoid_2048x22_bf16", 4099)]
+
+
+def grid_workload(name):
+    if name in WL:
+        return WL[name]
+    _, score, shape, *dt = name.split("_")
+    E, K = (int(v) for v in shape.split("x"))
+    wl = synth.sweep_workload(E, K, synth.SOFTMAX if score == "softmax" else synth.SIGMOID)
+    return dataclasses.replace(wl, dtype=synth.BF16) if dt else wl
 
 
 @pytest.mark.parametrize("name,T", GRID_CASES)
@@ -501,7 +514,7 @@ def test_grid_modes_identical(name, T):
     """The occupancy-sized persistent grid (waves loop over token groups;
     the grouped forward prefetches the next group) gives the same bits as
     one block per token group: forward, backward, aux scores."""
-    wl = WL[name]
+    wl = grid_workload(name)
     x_st, _ = wl.logits()
     g_st, _ = wl.grad()
     if T is not None:

@@ -156,13 +156,19 @@ constexpr int geo_split_row(const ColGeo &g, int w, int k, int row_lane)
 
 // Count kernel: 8 waves; CPL map bytes per lane and row with CPL the
 // largest of 16, 8 and 4 whose stripes cover E with at most 5% idle columns
-// (else the one that wastes least); row steps per split halved from 16
-// (down to 1) until the grid has kCountMinBlocks blocks.  Loss kernels: 4
-// waves, 4 elements per lane and row.
+// (else the one that wastes least).  Each column's total takes one atomic
+// per row split, and the atomics on one word queue behind each other when
+// the blocks finish together (about 20 ns each on MI355X: 512 of them made
+// the T=8192, E=512 count 15 us), so at most kCountMaxSplits splits share a
+// column; row steps per split are halved from 16 (down to 1) while the grid
+// has fewer than kCountMinBlocks blocks and the splits stay within that
+// cap, and blocks loop over the splits beyond it.  Loss kernels: 4 waves,
+// 4 elements per lane and row.
 constexpr int kCountWaves = 8;
 constexpr int kCountMaxSteps = 16;    // row steps per wave and split (map)
 constexpr int kCountMinBlocks = 512;
 constexpr int kCountMaxBlocks = 2048;
+constexpr int kCountMaxSplits = 64;   // row splits (atomics) per column
 constexpr int kLossWaves = kWaves;
 constexpr int kLossCpl = 2;           // log2 of 4 columns per lane
 constexpr int kLossSteps = 16;        // row steps per wave and split (scores)
@@ -188,11 +194,20 @@ inline int count_cpl_log2(int E)
 inline ColGeo count_geo(int64_t T, int E)
 {
     const int cl = count_cpl_log2(E);
+    auto geo = [&](int steps) {
+        ColGeo g = col_geo(T, E, kCountWaves, cl, steps, kCountMaxBlocks);
+        if (g.gsplit > kCountMaxSplits)
+            g.gsplit = kCountMaxSplits;
+        return g;
+    };
     int steps = kCountMaxSteps;
-    ColGeo g = col_geo(T, E, kCountWaves, cl, steps, kCountMaxBlocks);
+    ColGeo g = geo(steps);
     while (steps > 1 && (int64_t)g.gsplit * g.nstripe < kCountMinBlocks) {
+        const ColGeo h = geo(steps / 2);
+        if (h.nsplit > kCountMaxSplits)
+            break;
         steps /= 2;
-        g = col_geo(T, E, kCountWaves, cl, steps, kCountMaxBlocks);
+        g = h;
     }
     return g;
 }

@@ -650,8 +650,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.exit("bench.py: the router is benchmarked on one GPU; multi-GPU runs "
-                 "(--gpus > 1) are not part of this build")
+        sys.exit("bench.py: the router is benchmarked on one GPU only; --gpus above 1 "
+                 "is not supported (tokens shard with no exchange, so one GPU's share "
+                 "at its real shape is the measurement)")
 
     import numpy as np
     import torch

@@ -953,6 +953,15 @@ def main():
     if not args.only and args.workload == "c4_softmax_2304x36":
         out["stream_ceiling"] = {f"T{T}_E{E}": run_stream_ceiling(torch, router, T, E),
                                  "T8192_E256": run_stream_ceiling(torch, router, 8192, 256)}
+        # the dominant kernel against the two data-movement references of its
+        # own pass mix: what the pass's bytes take with no arithmetic
+        here = out["stream_ceiling"][f"T{T}_E{E}"]
+        refs = {"stream_mix_us": here[roof["passes"][0]]["us"]}
+        if roof["kernel"] == "fwd_kernel" and "topk_fwd_row_pattern" in here:
+            refs["row_pattern_us"] = here["topk_fwd_row_pattern"]["us"]
+        roof["ceilings"] = {k: v for k, v in refs.items()}
+        roof["ceilings"].update({k.replace("_us", "_frac"): round(v / roof["us_avg"], 4)
+                                 for k, v in refs.items()})
         out["stream_ceiling_note"] = (
             "the library's streaming kernel (16-byte non-temporal buffer loads and stores, no "
             "arithmetic) moving each pass's bytes at its read:write mix over T*E elements, "

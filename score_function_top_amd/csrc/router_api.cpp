@@ -246,9 +246,9 @@ hipError_t launch_bwd(const Cfg &c, int dtype, int score, const BwdParams &p, co
     return hipErrorInvalidValue;
 }
 
-unsigned grid_for(int64_t T, int lpt)
+unsigned grid_for(int64_t T, int lpt, int waves = kWaves)
 {
-    const int64_t tpb = (int64_t)kWaves * (64 / lpt);
+    const int64_t tpb = (int64_t)waves * (64 / lpt);
     int64_t blocks = (T + tpb - 1) / tpb;
     const int64_t cap = (int64_t)1 << 22;  // the kernels stride over the rest
     return (unsigned)(blocks < cap ? blocks : cap);
@@ -349,7 +349,8 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     // LDS of the launch: the candidate lists, plus the row copy of the LDS
     // group stage; a host-side bound first (the workgroup LDS the kernels
     // are built for), then the device's own limit
-    const int tpb = kWaves * (64 / c.lpt);
+    const int waves = fwd_waves(c.lpt, c.nch, gm, sel, c.vec);
+    const int tpb = waves * (64 / c.lpt);
     size_t smem = (size_t)tpb * cand_slots(c.lpt) * sizeof(uint64_t);
     if (gm == GROUP_LDS)
         smem += (size_t)tpb * group_scratch_floats(E, G, c.lpt) * sizeof(float);
@@ -378,7 +379,8 @@ router_status fwd_common(const void *x, int dtype, int64_t T, int32_t E, int32_t
     p.q = G > 0 ? K / Kg : 0;
     p.P = G > 0 ? E / G : 0;
     p.scale = scale;
-    const Launch l{grid_for(T, c.lpt), smem, (hipStream_t)stream, persistent()};
+    const Launch l{grid_for(T, c.lpt, waves), smem, (hipStream_t)stream, persistent(),
+                   (unsigned)(64 * waves)};
     return launch_fwd(c, dtype, score_fn, gm, p, l) == hipSuccess ? ROUTER_OK : ROUTER_ERR_HIP;
 }
 

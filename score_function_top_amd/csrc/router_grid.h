@@ -14,15 +14,17 @@
 
 namespace rker {
 
-// Resident blocks of kernel KERN on the current device for `smem` bytes of
-// dynamic LDS (times the compute units); 0 when the device cannot be
-// queried.  Cached per device and LDS size.
+// Resident blocks of kernel KERN on the current device for blocks of
+// `threads` threads and `smem` bytes of dynamic LDS (times the compute
+// units); 0 when the device cannot be queried.  Cached per device, LDS size
+// and block size.
 template <auto KERN>
-unsigned resident_blocks(size_t smem)
+unsigned resident_blocks(size_t smem, unsigned threads)
 {
     constexpr int kMaxDev = 64, kSlots = 8;
     struct Entry {
         size_t smem;
+        unsigned threads;
         unsigned blocks;
     };
     static std::mutex mu;
@@ -33,15 +35,16 @@ unsigned resident_blocks(size_t smem)
         return 0;
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < used[d]; i++)
-        if (cache[d][i].smem == smem)
+        if (cache[d][i].smem == smem && cache[d][i].threads == threads)
             return cache[d][i].blocks;
     int occ = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERN, kBlock, smem) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERN, (int)threads, smem) !=
+            hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess)
         return 0;
     const unsigned blocks = (unsigned)(occ > 0 ? occ : 1) * (unsigned)cus;
     if (used[d] < kSlots)
-        cache[d][used[d]++] = Entry{smem, blocks};
+        cache[d][used[d]++] = Entry{smem, threads, blocks};
     return blocks;
 }
 
@@ -52,7 +55,7 @@ unsigned launch_grid(const Launch &l)
 {
     if (!l.persistent)
         return l.grid;
-    const unsigned cap = resident_blocks<KERN>(l.smem);
+    const unsigned cap = resident_blocks<KERN>(l.smem, l.threads);
     return cap > 0 && l.grid > cap ? cap : l.grid;
 }
 

@@ -714,13 +714,14 @@ __device__ __forceinline__ float group_limit_reg(float (&key)[NCH][4], const flo
 // pruned sort, or the bit search when p.sel == SEL_BITS.  GM selects
 // group-limited routing (p.G > 0): GROUP_NONE, GROUP_LDS (group_limit, any
 // P) or GROUP_REG (group_limit_reg, groups that tile the chunks).
-template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC>
-__global__ void __launch_bounds__(kBlock, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
+template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC,
+          int WPB = kWaves>
+__global__ void __launch_bounds__(64 * WPB, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
                                                  : (GM == GROUP_REG ? (NCH <= 2 && LPT >= 32 ? 5 : 4) : 1))
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave
-    constexpr int TPB = kWaves * GPW;        // tokens per block
+    constexpr int TPB = WPB * GPW;           // tokens per block (WPB waves)
     constexpr int VPL = NCH * 4;
     extern __shared__ uint64_t smem[];
 

@@ -33,8 +33,12 @@ hipError_t fwd_sel(const FwdParams &p, int gm, const Launch &l)
             return hipErrorInvalidValue;
         }
     } else {
-        constexpr auto k = fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_NONE, VEC>;
-        hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), b, l.smem, l.stream, p);
+        // waves per block as the host sized the grid and LDS for
+        constexpr int W = fwd_waves(LPT, NCH, GROUP_NONE, SEL, VEC);
+        if (l.threads != 64u * W)
+            return hipErrorInvalidValue;
+        constexpr auto k = fwd_kernel<LPT, NCH, TIn, SCORE, SEL, GROUP_NONE, VEC, W>;
+        hipLaunchKernelGGL(k, dim3(launch_grid<k>(l)), dim3(64 * W), l.smem, l.stream, p);
     }
     return hipGetLastError();
 }

@@ -87,7 +87,23 @@ struct Launch {
     size_t smem;
     hipStream_t stream;
     bool persistent;     // cap the grid at the kernel's resident blocks
+    unsigned threads = kBlock;
 };
+
+// Waves per block of a forward kernel.  The pruned forwards of 64-lane rows
+// of 6..9 chunks (1024 < E <= 2304 on the vector path) run one wave (one
+// token) per block: their 198-VGPR waves fit 2 per SIMD, and with
+// single-wave blocks the dispatcher refills a slot as soon as its token is
+// done instead of when the block's slowest of four is (T=8192: E=2304, K=36
+// 45.5 -> 44.3 us; E=1536, K=8 30.0 -> 29.3 us).  Every other forward keeps
+// 4 waves: 1-wave blocks made the 16- and 32-lane kernels slower (E=256 and
+// E=512 forwards 6 and 10% on the same machine).
+constexpr int fwd_waves(int lpt, int nch, int gm, int sel, bool vec)
+{
+    return lpt == 64 && nch >= 6 && nch <= 9 && gm == GROUP_NONE && sel != SEL_ARGMAX && vec
+               ? 1
+               : kWaves;
+}
 
 // Column-stripe geometry of the aux-loss kernels (tokens per expert, the
 // loss and its gradient).  Lane l of a wave owns CPL = 1 << cpl_log2

@@ -91,16 +91,18 @@ struct Launch {
 };
 
 // Waves per block of a forward kernel.  The pruned forwards of 64-lane rows
-// of 6..9 chunks (1024 < E <= 2304 on the vector path) run one wave (one
-// token) per block: their 198-VGPR waves fit 2 per SIMD, and with
-// single-wave blocks the dispatcher refills a slot as soon as its token is
-// done instead of when the block's slowest of four is (T=8192: E=2304, K=36
-// 45.5 -> 44.3 us; E=1536, K=8 30.0 -> 29.3 us).  Every other forward keeps
-// 4 waves: 1-wave blocks made the 16- and 32-lane kernels slower (E=256 and
-// E=512 forwards 6 and 10% on the same machine).
+// of 6..12 chunks (1024 < E <= 3072 on the vector path) run one wave (one
+// token) per block: their waves fit only 2 per SIMD, and with single-wave
+// blocks the dispatcher refills a slot as soon as its token is done instead
+// of when the block's slowest of four is (T=8192: E=2304, K=36 45.5 ->
+// 44.3 us; E=1536, K=8 30.0 -> 29.3 us; E=3072, K=8 59.2 -> 56.5 us).  Every
+// other forward keeps 4 waves: measured on the same machine, 1-wave blocks
+// made the 16- and 32-lane kernels slower (E=256 and E=512 forwards by 6
+// and 10%), and the 3- and 16-chunk rows and the argmax path (K=1 at
+// E=2304) by 1-3%; 2-wave blocks gave half the gain at E=2304.
 constexpr int fwd_waves(int lpt, int nch, int gm, int sel, bool vec)
 {
-    return lpt == 64 && nch >= 6 && nch <= 9 && gm == GROUP_NONE && sel != SEL_ARGMAX && vec
+    return lpt == 64 && nch >= 6 && nch <= 12 && gm == GROUP_NONE && sel != SEL_ARGMAX && vec
                ? 1
                : kWaves;
 }

@@ -158,6 +158,8 @@ EDGE = [
     (50, 4096, 1, synth.SIGMOID), (40, 4096, 100, synth.SOFTMAX), (31, 2304, 64, synth.SOFTMAX),
     (31, 2304, 65, synth.SOFTMAX), (19, 2000, 2000, synth.SOFTMAX), (300, 512, 33, synth.SIGMOID),
     (300, 256, 17, synth.SOFTMAX), (300, 128, 64, synth.SOFTMAX),
+    # one-wave blocks: 6- and 12-chunk rows, with a partial last row batch
+    (1029, 1536, 8, synth.SOFTMAX), (517, 3072, 20, synth.SIGMOID),
 ]
 
 
@@ -497,7 +499,8 @@ def test_path_parity(T, E, K, sf, b, G):
 GRID_CASES = [("c4_softmax_2304x36", None), ("c4_softmax_2304x36", 6001),
               ("c5_group_sigmoid_256x8_bf16", None),
               ("c2_softmax_256x4", None), ("c3_sigmoid_512x22", 4097),
-              ("sweep_softmax_1536x8", 5003), ("sweep_sigmoid_2048x22_bf16", 4099)]
+              ("sweep_softmax_1536x8", 5003), ("sweep_sigmoid_2048x22_bf16", 4099),
+              ("sweep_softmax_3072x8", 3001)]
 
 
 def grid_workload(name):

@@ -968,21 +968,26 @@ bwd_kernel(BwdParams p)
     constexpr int TPB = kWaves * GPW;
 
     const int lane64 = lane_id();
-    const int lane = lane64 & (LPT - 1);
-    const int j_lane = 4 * lane;
+    const int lane0 = lane64 & (LPT - 1);
     const int grp = lane64 / LPT;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int E = p.E;
     const uint32_t goff = (uint32_t)(grp * E);
     const bool aux = p.m == nullptr;
     const bool renorm_mode = p.renorm && (SCORE == SCORE_SOFTMAX ? !aux : (aux || p.K > 1));
-    const bool need_b = SCORE == SCORE_SOFTMAX || renorm_mode;
     const float c0 = aux ? 1.0f : p.scale;
     const float mask_w = (SCORE == SCORE_SOFTMAX && !renorm_mode) ? 0.0f : 1.0f;
     const float mask_g = 1.0f - mask_w;
 
     for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
          tb += (int64_t)gridDim.x * TPB) {
+        // rows of 12 and 16 chunks: an opaque copy of the lane index per
+        // iteration keeps the per-chunk offsets and range masks out of
+        // registers held across the token loop
+        int lane = lane0;
+        if constexpr (NCH >= 12)
+            asm volatile("" : "+v"(lane));
+        const int j_lane = 4 * lane;
         const int64_t t0 = tb + wave * GPW;
         const int64_t left = p.T - t0;
         const int nval = left <= 0 ? 0 : (left >= GPW ? GPW : (int)left);
@@ -1008,32 +1013,37 @@ bwd_kernel(BwdParams p)
             for (int c = 0; c < NCH; c++)
                 mw[c] = 0x01010101u;
         }
-        float A = 1.0f, B = 0.0f;
-        if (renorm_mode || need_b) {
-            float pa[NCH], pb[NCH];
+        // A and B, and the mode chosen by selects.  With the sigmoid a
+        // branch on the mode here let the compiler sink the g and s loads
+        // below it, behind a wait for the map (two round trips per row, the
+        // map bytes expanded twice, 236 VGPRs at 9 chunks; E=4096, K=16:
+        // 152 -> 74 us), so its A and B are always computed.  The softmax
+        // needs B always and A for renormalisation only; its branch is
+        // harmless (the loads stay above it) and skips a reduction.
+        float pa[NCH], pb[NCH];
 #pragma unroll
-            for (int c = 0; c < NCH; c++) {
-                float a4[4], b4[4];
+        for (int c = 0; c < NCH; c++) {
+            float a4[4], b4[4];
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    a4[u] = ((mw[c] >> (8 * u)) & 0xFFu) ? s[c][u] : 0.0f;
-                    b4[u] = g[c][u] * a4[u];
-                }
-                pa[c] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-                pb[c] = (b4[0] + b4[1]) + (b4[2] + b4[3]);
+            for (int u = 0; u < 4; u++) {
+                a4[u] = ((mw[c] >> (8 * u)) & 0xFFu) ? s[c][u] : 0.0f;
+                b4[u] = g[c][u] * a4[u];
             }
+            pa[c] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+            pb[c] = (b4[0] + b4[1]) + (b4[2] + b4[3]);
+        }
+        float A = 1.0f;
+        if constexpr (SCORE == SCORE_SOFTMAX) {
             if (renorm_mode)
                 A = group_sum<LPT>(tree_sum<NCH>(pa));
-            if (need_b)
-                B = group_sum<LPT>(tree_sum<NCH>(pb));
+        } else {
+            A = group_sum<LPT>(tree_sum<NCH>(pa));
         }
-        float alpha = c0, beta = SCORE == SCORE_SOFTMAX ? B : 0.0f;
-        if (renorm_mode) {
-            const float rA0 = 1.0f / A;  // every lane: no divergent branch
-            const float rA = Ev ? rA0 : 0.0f;
-            alpha = c0 * rA;
-            beta = B * rA;
-        }
+        const float B = group_sum<LPT>(tree_sum<NCH>(pb));
+        const float rA0 = 1.0f / A;  // every lane: no divergent branch
+        const float rA = Ev ? rA0 : 0.0f;
+        const float alpha = renorm_mode ? c0 * rA : c0;
+        const float beta = renorm_mode ? B * rA : (SCORE == SCORE_SOFTMAX ? B : 0.0f);
         const rsrc_t rd = make_rsrc(static_cast<TIn *>(p.dx) + off0, nel * io<TIn>::kSize);
 #pragma unroll
         for (int c = 0; c < NCH; c++) {

@@ -780,7 +780,12 @@ fwd_kernel(FwdParams p)
     uint64_t *cand = smem + gslot * cand_slots(LPT);
     const int E = p.E;
     const uint32_t goff = (uint32_t)(grp * E);             // group row in the wave buffer
-    const bool has_bias = p.bias != nullptr;
+    // The host takes an expert bias with the sigmoid only.  The softmax
+    // rows of 16 chunks drop the bias code at compile time, which freed
+    // registers they need (T=8192, E=4096, K=36: 136 -> 90 us); narrower
+    // softmax rows keep the run-time test, which measured faster there
+    // (E=512, K=8: 9.8 against 10.7 us; E=3072: 56.6 against 57.4 us).
+    const bool has_bias = (SCORE == SCORE_SIGMOID || NCH < 16) && p.bias != nullptr;
 
     for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
          tb += (int64_t)gridDim.x * TPB) {

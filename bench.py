@@ -524,7 +524,13 @@ def copy_calibration(torch, dev, mib):
 
 # Read:write bytes per element of each pass (fp32), for the same-mix ceiling.
 STREAM_MIX = {"topk_fwd": (4, 9), "topk_bwd": (9, 4), "aux_fwd": (4, 9), "aux_bwd": (8, 4),
-              "copy": (4, 4), "read_only": (4, 0), "write_only": (0, 4)}
+              "copy": (4, 4), "read_only": (4, 0), "write_only": (0, 4),
+              "map_read": (1, 0)}
+# the stream mix whose bytes equal each aux-loss pass's (fp32 scores): the
+# count reads the byte map, the loss reads the scores, its gradient writes
+# them (the per-expert vectors are a few KB)
+LOSS_STREAM = {"tokens_per_expert": "map_read", "aux_loss_fwd": "read_only",
+               "aux_loss_bwd": "write_only"}
 
 
 def run_stream_ceiling(torch, router, T, E):
@@ -962,11 +968,18 @@ def main():
         roof["ceilings"] = {k: v for k, v in refs.items()}
         roof["ceilings"].update({k.replace("_us", "_frac"): round(v / roof["us_avg"], 4)
                                  for k, v in refs.items()})
+        if "aux_loss" in out and esz == 4:
+            for kind, mix in LOSS_STREAM.items():
+                c = here[mix]["us"]
+                out["aux_loss"][kind]["stream_ceiling_us"] = c
+                out["aux_loss"][kind]["stream_ceiling_frac"] = round(
+                    c / out["aux_loss"][kind]["us_graph"], 4)
         out["stream_ceiling_note"] = (
             "the library's streaming kernel (16-byte non-temporal buffer loads and stores, no "
             "arithmetic) moving each pass's bytes at its read:write mix over T*E elements, "
             "cold; the bandwidth a kernel with that mix can reach on this device, at the "
-            "headline size and at the E=256 sweep cells' size; topk_fwd_row_pattern moves "
+            "headline size and at the E=256 sweep cells' size (map_read: the byte map, the "
+            "tokens-per-expert pass's bytes); topk_fwd_row_pattern moves "
             "the forward's bytes in the forward's own pattern (one wave per row, the row read "
             "whole, then two fp32 rows and a byte row written), no arithmetic")
     if not args.no_sweep and not args.only:

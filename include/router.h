@@ -391,13 +391,16 @@ router_status router_device_query(int32_t *compute_units, int32_t *clock_khz,
  * measurement, like router_device_query).  Reads read_bytes from src and
  * writes write_bytes to dst (device pointers, 16-byte aligned, sizes
  * multiples of 16) with the router kernels' access style and no other
- * work; timing it at a kernel's read:write mix gives the bandwidth this
- * device reaches for that mix.  dst receives arbitrary contents.  Errors:
- * negative or unaligned sizes, null or misaligned pointers INVALID_ARG.
+ * work, each thread moving units_per_thread 16-byte units (1, 2, 4 or 8)
+ * with every load issued before its stores; the fastest of these at a
+ * kernel's read:write mix gives the bandwidth this device reaches for that
+ * mix.  The first min(read_bytes, write_bytes) bytes of dst receive src;
+ * the rest arbitrary contents.  Errors: negative or unaligned sizes, null
+ * or misaligned pointers, another units_per_thread INVALID_ARG.
  */
 router_status router_stream_bandwidth(const void *src, int64_t read_bytes,
                                       void *dst, int64_t write_bytes,
-                                      void *hip_stream);
+                                      int32_t units_per_thread, void *hip_stream);
 
 /*
  * Bandwidth reference in the forward's own access pattern (no passage:

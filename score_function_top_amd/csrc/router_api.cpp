@@ -752,14 +752,19 @@ router_status router_device_query(int32_t *compute_units, int32_t *clock_khz,
 }
 
 router_status router_stream_bandwidth(const void *src, int64_t read_bytes, void *dst,
-                                      int64_t write_bytes, void *hip_stream)
+                                      int64_t write_bytes, int32_t units_per_thread,
+                                      void *hip_stream)
 {
     if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 != 0 || write_bytes % 16 != 0)
+        return ROUTER_ERR_INVALID_ARG;
+    if (units_per_thread != 1 && units_per_thread != 2 && units_per_thread != 4 &&
+        units_per_thread != 8)
         return ROUTER_ERR_INVALID_ARG;
     if ((read_bytes > 0 && (!src || !aligned(src, 16))) ||
         (write_bytes > 0 && (!dst || !aligned(dst, 16))))
         return ROUTER_ERR_INVALID_ARG;
-    return launch_stream(src, read_bytes, dst, write_bytes, (hipStream_t)hip_stream) == hipSuccess
+    return launch_stream(src, read_bytes, dst, write_bytes, units_per_thread,
+                         (hipStream_t)hip_stream) == hipSuccess
                ? ROUTER_OK
                : ROUTER_ERR_HIP;
 }

@@ -348,7 +348,7 @@ bool fwd_grouped32(int lpt, int nch, int dtype, int score, int Q, bool bias,
 
 // Streaming kernel for the bandwidth ceiling (router_stream.hip).
 hipError_t launch_stream(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes,
-                         hipStream_t stream);
+                         int units, hipStream_t stream);
 hipError_t launch_row_stream(const float *x, float *a, float *b, uint8_t *m, int64_t T, int E,
                              hipStream_t stream);
 

@@ -2,9 +2,9 @@
 // references next to the router's measured bandwidth, with no arithmetic:
 //   stream_kernel reads `read_bytes` and writes `write_bytes` with the
 //     access style of the router kernels (16-byte buffer loads and stores
-//     per lane, non-temporal), one 16-byte unit per thread, so a run at the
-//     router's read:write mix gives the bandwidth this device reaches for
-//     that mix;
+//     per lane, non-temporal), 1, 2, 4 or 8 16-byte units per thread, so
+//     the fastest of these runs at the router's read:write mix gives the
+//     bandwidth this device reaches for that mix;
 //   row_stream_kernel moves the forward's bytes in the forward's own
 //     pattern (one wave per row, the row loaded whole, then three stores
 //     per chunk), which is what the forward can reach at best.
@@ -21,25 +21,38 @@ namespace {
 
 // Unit u (16 bytes): src unit u is read when u < nr, dst unit u written when
 // u < nw; a written unit holds the unit read at u (or the unit index), so
-// every load feeds a store and none is dead code.
+// every load feeds a store and none is dead code.  A thread moves U units
+// per step (units i*kBlock + tid of its block's window, every load issued
+// before any store): one unit per thread leaves a wave 1 KB in flight, too
+// little for a read-heavy mix to reach the bandwidth the router kernels
+// reach with a whole row in flight (T=8192, E=2304: read only 14.8 us at
+// U=1, 12.1 at U=4; the 4:9 write-heavy mix is fastest at U=1).
+template <int U>
 __global__ __launch_bounds__(kBlock) void stream_kernel(const void *src, int64_t nr, void *dst,
                                                         int64_t nw)
 {
+    constexpr int64_t kSpan = (int64_t)kBlock * U;  // units per block and step
     const int64_t n = nr > nw ? nr : nw;
-    const int64_t step = (int64_t)gridDim.x * kBlock;
-    for (int64_t u0 = (int64_t)blockIdx.x * kBlock; u0 < n; u0 += step) {
-        // one buffer window of kBlock units per block and step: offsets
+    const int64_t step = (int64_t)gridDim.x * kSpan;
+    for (int64_t u0 = (int64_t)blockIdx.x * kSpan; u0 < n; u0 += step) {
+        // one buffer window of kSpan units per block and step: offsets
         // stay 32-bit; units past nr / nw fall outside and are dropped
-        const int64_t rr = nr - u0 < kBlock ? (nr > u0 ? nr - u0 : 0) : kBlock;
-        const int64_t ww = nw - u0 < kBlock ? (nw > u0 ? nw - u0 : 0) : kBlock;
+        const int64_t rr = nr - u0 < kSpan ? (nr > u0 ? nr - u0 : 0) : kSpan;
+        const int64_t ww = nw - u0 < kSpan ? (nw > u0 ? nw - u0 : 0) : kSpan;
         const rsrc_t rs = make_rsrc((const char *)src + (rr ? u0 * 16 : 0), (uint32_t)(rr * 16));
         const rsrc_t rd = make_rsrc((char *)dst + (ww ? u0 * 16 : 0), (uint32_t)(ww * 16));
-        const uint32_t off = threadIdx.x * 16u;
-        float v[4];
-        io<float>::load4(rs, off, 0, v);
-        if (u0 + (int64_t)threadIdx.x >= nr)
-            v[0] = (float)(u0 + threadIdx.x);
-        io<float>::store4(rd, off, v);
+        float v[U][4];
+#pragma unroll
+        for (int i = 0; i < U; i++)
+            io<float>::load4(rs, (uint32_t)(i * kBlock + (int)threadIdx.x) * 16u, 0, v[i]);
+        __builtin_amdgcn_sched_barrier(0);  // every load in flight before any store
+#pragma unroll
+        for (int i = 0; i < U; i++) {
+            const int64_t u = u0 + i * kBlock + (int64_t)threadIdx.x;
+            if (u >= nr)
+                v[i][0] = (float)u;
+            io<float>::store4(rd, (uint32_t)(i * kBlock + (int)threadIdx.x) * 16u, v[i]);
+        }
     }
 }
 
@@ -113,17 +126,24 @@ hipError_t launch_row_stream(const float *x, float *a, float *b, uint8_t *m, int
 }
 
 hipError_t launch_stream(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes,
-                         hipStream_t stream)
+                         int units, hipStream_t stream)
 {
     const int64_t nr = read_bytes / 16, nw = write_bytes / 16;
     const int64_t n = nr > nw ? nr : nw;
     if (n == 0)
         return hipSuccess;
-    int64_t blocks = (n + kBlock - 1) / kBlock;
+    const int64_t span = (int64_t)kBlock * units;
+    int64_t blocks = (n + span - 1) / span;
     if (blocks > 65536)
         blocks = 65536;
-    hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, src, nr,
-                       dst, nw);
+    const dim3 grid((unsigned)blocks), block(kBlock);
+    switch (units) {
+    case 1: hipLaunchKernelGGL(stream_kernel<1>, grid, block, 0, stream, src, nr, dst, nw); break;
+    case 2: hipLaunchKernelGGL(stream_kernel<2>, grid, block, 0, stream, src, nr, dst, nw); break;
+    case 4: hipLaunchKernelGGL(stream_kernel<4>, grid, block, 0, stream, src, nr, dst, nw); break;
+    case 8: hipLaunchKernelGGL(stream_kernel<8>, grid, block, 0, stream, src, nr, dst, nw); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ def load():
     lib.router_set_grid_mode.restype = ci
     lib.router_get_grid_mode.argtypes = []
     lib.router_get_grid_mode.restype = ci
-    lib.router_stream_bandwidth.argtypes = [vp, i64, vp, i64, vp]
+    lib.router_stream_bandwidth.argtypes = [vp, i64, vp, i64, ci, vp]
     lib.router_stream_bandwidth.restype = ci
     lib.router_row_stream_bandwidth.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.router_row_stream_bandwidth.restype = ci
@@ -133,12 +133,13 @@ GROUP_STAGE_AUTO = 0
 GROUP_STAGE_LDS = 1
 
 
-def stream_bandwidth(src, read_bytes, dst, write_bytes):
+def stream_bandwidth(src, read_bytes, dst, write_bytes, units=1):
     """Reads read_bytes of src and writes write_bytes of dst (uint8 GPU
-    tensors) with the router kernels' access style and no other work: the
-    bandwidth reference of a read:write mix (a measurement utility)."""
+    tensors) with the router kernels' access style and no other work,
+    `units` 16-byte units per thread (1, 2, 4 or 8): the bandwidth reference
+    of a read:write mix (a measurement utility)."""
     check(load().router_stream_bandwidth(_ptr(src), int(read_bytes), _ptr(dst),
-                                         int(write_bytes), _stream(src)))
+                                         int(write_bytes), int(units), _stream(src)))
 
 
 def row_stream_bandwidth(x, out_a, out_b, out_map):

@@ -10,14 +10,18 @@ from score_function_top_amd import router
 pytestmark = pytest.mark.gpu
 
 
-def test_stream_copies_the_read_part():
-    g = torch.Generator(DEV).manual_seed(11)
-    src = torch.randint(0, 256, (4096,), dtype=torch.uint8, device=DEV, generator=g)
-    dst = torch.zeros(8192, dtype=torch.uint8, device=DEV)
-    say("[bandwidth refs] stream 4096 read, 8192 written")
-    router.stream_bandwidth(src, 4096, dst, 8192)
+@pytest.mark.parametrize("units", [1, 2, 4, 8])
+@pytest.mark.parametrize("rb,wb", [(4096, 8192), (8192, 4096), (65536 + 48, 16 * 40000),
+                                   (0, 4096), (4096, 0)])
+def test_stream_copies_the_read_part(units, rb, wb):
+    g = torch.Generator(DEV).manual_seed(11 + units)
+    src = torch.randint(0, 256, (max(rb, 16),), dtype=torch.uint8, device=DEV, generator=g)
+    dst = torch.zeros(max(wb, 16), dtype=torch.uint8, device=DEV)
+    say(f"[bandwidth refs] stream {rb} read, {wb} written, {units} units per thread")
+    router.stream_bandwidth(src, rb, dst, wb, units)
     torch.cuda.synchronize()
-    assert torch.equal(dst[:4096], src)
+    n = min(rb, wb)
+    assert torch.equal(dst[:n], src[:n])
 
 
 @pytest.mark.parametrize("T,E", [(37, 256), (37, 2304), (5, 4096), (0, 512)])

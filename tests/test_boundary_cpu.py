@@ -337,11 +337,15 @@ def test_bandwidth_reference_host_checks():
     """The two data-movement references reject bad sizes and pointers on
     the host; T = 0 or empty sizes launch nothing."""
     lib = router.load()
-    assert lib.router_stream_bandwidth(P, 15, P, 16, None) == INV
-    assert lib.router_stream_bandwidth(P, -16, P, 16, None) == INV
-    assert lib.router_stream_bandwidth(None, 16, P, 16, None) == INV
-    assert lib.router_stream_bandwidth(P + 8, 16, P, 16, None) == INV
-    assert lib.router_stream_bandwidth(None, 0, None, 0, None) == OK
+    st = lib.router_stream_bandwidth
+    assert st(P, 15, P, 16, 1, None) == INV
+    assert st(P, -16, P, 16, 1, None) == INV
+    assert st(None, 16, P, 16, 1, None) == INV
+    assert st(P + 8, 16, P, 16, 1, None) == INV
+    for units in (0, 3, 16, -1):
+        assert st(P, 16, P, 16, units, None) == INV, units
+    for units in (1, 2, 4, 8):
+        assert st(None, 0, None, 0, units, None) == OK, units
     row = lib.router_row_stream_bandwidth
     for T, E in ((8, 255), (8, 300), (8, 4352), (8, 0), (-1, 256)):
         assert row(P, P, P, P, T, E, None) == INV, (T, E)

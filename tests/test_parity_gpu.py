@@ -253,7 +253,8 @@ def _random_cases(n=48, seed=2024):
 
 
 @pytest.mark.parametrize("T,E,K,sf,renorm,b,G,Kg,dtype,seed",
-                         _random_cases() + _random_cases(48, 2025))
+                         _random_cases() + _random_cases(48, 2025) + _random_cases(150, 7001) +
+                         _random_cases(150, 7002) + _random_cases(150, 7003))
 def test_random_configs(T, E, K, sf, renorm, b, G, Kg, dtype, seed):
     """Forward and backward against the oracle on seeded random shapes.  The
     backward reference uses the GPU's map: it equals the oracle's except on

@@ -760,10 +760,22 @@ __device__ __forceinline__ float group_limit_reg(float (&key)[NCH][4], const flo
 // pruned sort, or the bit search when p.sel == SEL_BITS.  GM selects
 // group-limited routing (p.G > 0): GROUP_NONE, GROUP_LDS (group_limit, any
 // P) or GROUP_REG (group_limit_reg, groups that tile the chunks).
+//
+// Rows of 16 chunks (3072 < E <= 4096) take the lane index through an
+// opaque copy in every token iteration: otherwise the per-chunk offsets and
+// range tests derived from it were hoisted out of the token loop and held
+// in about 40 registers for the kernel's life, which left one wave per
+// SIMD (softmax 306 -> 256 VGPRs, 2 waves per SIMD; T=8192, E=4096: 89.9 ->
+// 83.6 us).  The sigmoid rows (262 VGPRs with the copy) also ask for 2
+// waves per SIMD, which they reach without scratch (92.9 -> 84.2 us); the
+// softmax rows ran slower with that request (92.6 us), and rows of 12
+// chunks slower with the copy (E=3072 softmax: 56.3 -> 58.1 us).
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC,
           int WPB = kWaves>
-__global__ void __launch_bounds__(64 * WPB, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
-                                                 : (GM == GROUP_REG ? (NCH <= 2 && LPT >= 32 ? 5 : 4) : 1))
+__global__ void __launch_bounds__(
+    64 * WPB, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
+              : GM == GROUP_REG ? (NCH <= 2 && LPT >= 32 ? 5 : 4)
+              : (GM == GROUP_NONE && NCH == 16 && VEC && SCORE == SCORE_SIGMOID ? 2 : 1))
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave
@@ -772,8 +784,7 @@ fwd_kernel(FwdParams p)
     extern __shared__ uint64_t smem[];
 
     const int lane64 = lane_id();
-    const int lane = lane64 & (LPT - 1);
-    const int j_lane = 4 * lane;
+    const int lane0 = lane64 & (LPT - 1);
     const int grp = lane64 / LPT;                          // group in wave
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gslot = wave * GPW + grp;                    // group in block
@@ -789,6 +800,10 @@ fwd_kernel(FwdParams p)
 
     for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
          tb += (int64_t)gridDim.x * TPB) {
+        int lane = lane0;
+        if constexpr (NCH >= 16)
+            asm volatile("" : "+v"(lane));  // per iteration: see above
+        const int j_lane = 4 * lane;
         const int64_t t0 = tb + wave * GPW;                // first token of the wave
         const int64_t left = p.T - t0;
         const int nval = left <= 0 ? 0 : (left >= GPW ? GPW : (int)left);

@@ -64,7 +64,7 @@ PAGE_B300_GBPS = {"topk_fwd": 964, "topk_bwd": 2766, "aux_fwd": 891, "aux_bwd": 
 _ROUTER_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_kernels.h",
                    "router_launch.h", "router_params.h", "router_lpt16.hip", "router_lpt32.hip",
                    "router_lpt64a.hip", "router_lpt64b.hip", "router_lpt64c.hip",
-                   "router_scalar.hip"]
+                   "router_scalar.hip", "router_scalar2.hip"]
 _LOSS_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",
                  "router_loss.hip"]
 _GATE_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",

@@ -21,7 +21,7 @@ ARCH = os.environ.get("ROUTER_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["router_api.cpp", "router_lpt16.hip", "router_lpt32.hip",
            "router_lpt64a.hip", "router_lpt64b.hip", "router_lpt64c.hip",
-           "router_scalar.hip", "router_loss.hip", "router_route.hip",
+           "router_scalar.hip", "router_scalar2.hip", "router_loss.hip", "router_route.hip",
            "router_gate.hip", "router_stream.hip", ("router_grouped.hip", 16),
            ("router_grouped.hip", 32)]
 

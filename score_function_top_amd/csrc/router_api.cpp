@@ -228,7 +228,8 @@ hipError_t launch_fwd(const Cfg &c, int dtype, int score, int gm, const FwdParam
         fwd_lpt64a(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
         fwd_lpt64b(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
         fwd_lpt64c(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
-        fwd_scalar(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err))
+        fwd_scalar(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err) ||
+        fwd_scalar2(c.lpt, c.nch, c.vec, dtype, score, gm, p, l, &err))
         return err;
     return hipErrorInvalidValue;
 }
@@ -241,7 +242,8 @@ hipError_t launch_bwd(const Cfg &c, int dtype, int score, const BwdParams &p, co
         bwd_lpt64a(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
         bwd_lpt64b(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
         bwd_lpt64c(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
-        bwd_scalar(c.lpt, c.nch, c.vec, dtype, score, p, l, &err))
+        bwd_scalar(c.lpt, c.nch, c.vec, dtype, score, p, l, &err) ||
+        bwd_scalar2(c.lpt, c.nch, c.vec, dtype, score, p, l, &err))
         return err;
     return hipErrorInvalidValue;
 }

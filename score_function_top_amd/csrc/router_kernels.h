@@ -81,9 +81,9 @@ __device__ __forceinline__ void load_chunk(rsrc_t r, uint32_t goff, int c, int j
 
 // load_chunk in two halves, so that a row's loads can all be issued before
 // the first wait: load_chunk_raw requests the chunk as stored (a masked
-// access reads 0; bf16 stays two packed words in v[0], v[1]), and
-// mask_chunk, after the loads, unpacks it and applies the padding value.
-// Element-wise rows load and mask in load_chunk_raw.
+// access reads 0; bf16 stays two packed words in v[0], v[1]; element-wise
+// rows get their values), and mask_chunk, after the loads, unpacks it and
+// applies the padding value.
 template <int LPT, typename T, bool VEC, int POL = kStream>
 __device__ __forceinline__ void load_chunk_raw(rsrc_t r, uint32_t goff, int c, int j_lane,
                                                int Ev, float pad, float (&v)[4])
@@ -103,7 +103,13 @@ __device__ __forceinline__ void load_chunk_raw(rsrc_t r, uint32_t goff, int c, i
                 v[u] = as_f(t[u]);
         }
     } else {
-        load_chunk<LPT, T, VEC, POL>(r, goff, c, j_lane, Ev, pad, v);
+        // element-wise: masked elements read 0 (offset kOOB); the padding
+        // value goes in after every load is in flight (mask_chunk)
+        const int j0 = jrel<LPT>(c, 0) + j_lane;
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            v[u] = io<T>::template load1<POL>(
+                r, j0 + u < Ev ? (goff + (uint32_t)(j0 + u)) * io<T>::kSize : kOOB);
     }
 }
 
@@ -122,6 +128,11 @@ __device__ __forceinline__ void mask_chunk(int c, int j_lane, int Ev, float pad,
 #pragma unroll
         for (int u = 0; u < 4; u++)
             v[u] = ok ? v[u] : pad;
+    } else {
+        const int j0 = jrel<LPT>(c, 0) + j_lane;
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            v[u] = j0 + u < Ev ? v[u] : pad;
     }
 }
 
@@ -820,8 +831,10 @@ fwd_kernel(FwdParams p)
         // the later loads were issued.  Measured at T=8192 on one machine:
         // E=1792 38.1 -> 35.4 us, E=2048 40.1 -> 38.7, E=2304 44.4 -> 44.0;
         // at 6 and 12 chunks it was 3-5% slower, so they keep the plain load.
+        // The element-wise rows do the same at every width (E=4094: 356 ->
+        // 205 us; no change at 4 to 12 chunks).
         float key[NCH][4];
-        constexpr bool kRaw = VEC && LPT == 64 && NCH >= 8 && NCH <= 9;
+        constexpr bool kRaw = (VEC && LPT == 64 && NCH >= 8 && NCH <= 9) || !VEC;
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
             if constexpr (kRaw)
@@ -1090,10 +1103,17 @@ bwd_kernel(BwdParams p)
         }
         __builtin_amdgcn_sched_barrier(0);  // every load in flight before any math
         // aux: every expert routed (padding has s = g = 0 and adds nothing)
-        if (aux) {
+        // (element-wise rows: selects, no branch after the loads; see below)
+        if constexpr (VEC) {
+            if (aux) {
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+                    mw[c] = 0x01010101u;
+            }
+        } else {
 #pragma unroll
             for (int c = 0; c < NCH; c++)
-                mw[c] = 0x01010101u;
+                mw[c] = aux ? 0x01010101u : mw[c];
         }
         // A and B, and the mode chosen by selects.  With the sigmoid a
         // branch on the mode here let the compiler sink the g and s loads
@@ -1101,7 +1121,10 @@ bwd_kernel(BwdParams p)
         // map bytes expanded twice, 236 VGPRs at 9 chunks; E=4096, K=16:
         // 152 -> 74 us), so its A and B are always computed.  The softmax
         // needs B always and A for renormalisation only; its branch is
-        // harmless (the loads stay above it) and skips a reduction.
+        // harmless in the vector rows (the loads stay above it) and skips a
+        // reduction.  The element-wise rows compute A always and set the aux
+        // map by a select (T=8192, softmax, E=2302: 223.6 -> 133.8 us,
+        // E=3070: 152.7 -> 130.5, E=2046: 86.5 -> 81.0).
         float pa[NCH], pb[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
@@ -1115,7 +1138,7 @@ bwd_kernel(BwdParams p)
             pb[c] = (b4[0] + b4[1]) + (b4[2] + b4[3]);
         }
         float A = 1.0f;
-        if constexpr (SCORE == SCORE_SOFTMAX) {
+        if constexpr (SCORE == SCORE_SOFTMAX && VEC) {
             if (renorm_mode)
                 A = group_sum<LPT>(tree_sum<NCH>(pa));
         } else {

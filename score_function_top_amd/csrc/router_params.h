@@ -336,7 +336,7 @@ hipError_t launch_shared_gate(const GateParams &p, int dtype, bool vec_g, bool v
 constexpr int kNchLpt16[] = {1, 2, 4};
 constexpr int kNchLpt32[] = {1, 2, 4};
 constexpr int kNchLpt64[] = {1, 2, 3, 4, 6, 8, 9, 12, 16};
-constexpr int kNchScalar[] = {1, 2, 4, 8, 16};
+constexpr int kNchScalar[] = {1, 2, 3, 4, 6, 8, 9, 12, 16};
 
 // Group-limited forward for rows of 32-expert groups (router_grouped.h):
 // 16- or 32-lane tokens of 1, 2 or 4 chunks (E = nch * 4 * lpt), top lists
@@ -365,6 +365,7 @@ ROUTER_DECLARE_PART(lpt64a)
 ROUTER_DECLARE_PART(lpt64b)
 ROUTER_DECLARE_PART(lpt64c)
 ROUTER_DECLARE_PART(scalar)
+ROUTER_DECLARE_PART(scalar2)
 #undef ROUTER_DECLARE_PART
 
 }  // namespace rker

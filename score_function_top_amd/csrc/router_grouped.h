@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 6 : 4) grouped_fwd_kernel(F
                                     : (int)kOOB;
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
-            const int soff = (int)((uint32_t)jrel<LPT>(c, 0) * io<TIn>::kSize);
+            const int soff = (int)((uint32_t)jrel<LPT, true>(c, 0) * io<TIn>::kSize);
             if constexpr (BF)
                 dst[c] = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, kStream);
             else
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 6 : 4) grouped_fwd_kernel(F
 #pragma unroll
             for (int c = 0; c < NCH; c++) {
                 typedef float f4 __attribute__((ext_vector_type(4)));
-                const f4 b = *reinterpret_cast<const f4 *>(bl + jrel<LPT>(c, 0) + j_lane);
+                const f4 b = *reinterpret_cast<const f4 *>(bl + jrel<LPT, true>(c, 0) + j_lane);
 #pragma unroll
                 for (int u = 0; u < 4; u++)
                     key[c][u] = s[c][u] + b[u];
@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 6 : 4) grouped_fwd_kernel(F
         static_assert(G <= 16, "at most 16 groups");
 
         // ---- top-K among the kept groups
-        const Thresh t = select_prune<LPT, NCH, false, true>(key, p.K, lane, j_lane, cand, true,
+        const Thresh t = select_prune<LPT, NCH, false, true, true>(key, p.K, lane, j_lane, cand, true,
                                                               bound);
         // selection as 0/1 floats: the map bytes (one conversion per byte),
         // the renormalisation sum and the probs take them without selects
@@ -277,7 +277,7 @@ __global__ void __launch_bounds__(kBlock, NCH <= 2 ? 6 : 4) grouped_fwd_kernel(F
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     const float k = key[c][u];
-                    const int in = (int)(k > tx) | ((int)(k == tx) & (int)(jrel<LPT>(c, u) <= jt));
+                    const int in = (int)(k > tx) | ((int)(k == tx) & (int)(jrel<LPT, true>(c, u) <= jt));
                     mf[c][u] = in ? 1.0f : 0.0f;
                 }
         }

@@ -23,6 +23,7 @@ Prints one JSON line.  --gpus above 1 exits: this router is benchmarked on
 one GPU.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -626,14 +627,19 @@ def run_decode_route(torch, router, synth, steps):
 
 def workload_by_name(synth, name):
     """One of the five workloads, or a sweep cell named
-    sweep_<softmax|sigmoid>_<E>x<K> (T=8192)."""
+    sweep_<softmax|sigmoid>_<E>x<K> (T=8192; a _bf16 suffix stores the
+    logits and gradients in bf16)."""
     if name in synth.WORKLOADS:
         return synth.WORKLOADS[name]
     parts = name.split("_")
-    if len(parts) == 3 and parts[0] == "sweep" and parts[1] in ("softmax", "sigmoid"):
+    bf16 = len(parts) == 4 and parts[3] == "bf16"
+    if (len(parts) == 3 or bf16) and parts[0] == "sweep" and parts[1] in ("softmax", "sigmoid"):
         E, K = (int(v) for v in parts[2].split("x"))
-        return synth.sweep_workload(E, K, synth.SOFTMAX if parts[1] == "softmax"
-                                    else synth.SIGMOID)
+        wl = synth.sweep_workload(E, K, synth.SOFTMAX if parts[1] == "softmax"
+                                  else synth.SIGMOID)
+        if bf16:
+            wl = dataclasses.replace(wl, name=name, dtype=synth.BF16)
+        return wl
     raise SystemExit(f"bench.py: unknown workload {name}")
 
 

@@ -799,8 +799,10 @@ __device__ __forceinline__ float group_limit_reg(float (&key)[NCH][4], const flo
 // SIMD (softmax 306 -> 256 VGPRs, 2 waves per SIMD; T=8192, E=4096: 89.9 ->
 // 83.6 us).  The sigmoid rows (262 VGPRs with the copy) also ask for 2
 // waves per SIMD, which they reach without scratch (92.9 -> 84.2 us); the
-// softmax rows ran slower with that request (92.6 us), and rows of 12
-// chunks slower with the copy (E=3072 softmax: 56.3 -> 58.1 us).
+// softmax rows ran slower with that request (92.6 us).  The bf16 rows of
+// 12 chunks take the copy too (259 -> 208 VGPRs, 2 waves per SIMD; E=3072
+// bf16 softmax 70.2 -> 43.0 us, sigmoid 75.1 -> 47.3 us); the fp32 ones
+// ran slower with it (E=3072 softmax: 56.3 -> 58.1 us).
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC,
           int WPB = kWaves>
 __global__ void __launch_bounds__(
@@ -832,7 +834,7 @@ fwd_kernel(FwdParams p)
     for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
          tb += (int64_t)gridDim.x * TPB) {
         int lane = lane0;
-        if constexpr (NCH >= 16)
+        if constexpr (NCH >= 16 || (NCH >= 12 && sizeof(TIn) == 2))
             asm volatile("" : "+v"(lane));  // per iteration: see above
         const int j_lane = lane_part<VEC>(lane);
         const int64_t t0 = tb + wave * GPW;                // first token of the wave

@@ -800,15 +800,22 @@ __device__ __forceinline__ float group_limit_reg(float (&key)[NCH][4], const flo
 // 83.6 us).  The sigmoid rows (262 VGPRs with the copy) also ask for 2
 // waves per SIMD, which they reach without scratch (92.9 -> 84.2 us); the
 // softmax rows ran slower with that request (92.6 us).  The bf16 rows of
-// 12 chunks take the copy too (259 -> 208 VGPRs, 2 waves per SIMD; E=3072
-// bf16 softmax 70.2 -> 43.0 us, sigmoid 75.1 -> 47.3 us); the fp32 ones
-// ran slower with it (E=3072 softmax: 56.3 -> 58.1 us).
+// 6 chunks and more take the copy too, and those of 9 and 12 chunks ask
+// for 3 waves per SIMD (a bf16 row moves half the logit bytes, so the
+// same per-element arithmetic is less hidden and more rows in flight pay):
+// T=8192, bf16 softmax E=1536 25.2 -> 23.5 us, E=2048 33.7 -> 29.3,
+// E=2304 38.4 -> 32.4 (K=36; sigmoid 41.1 -> 33.4), E=3072 70.2 -> 43.1
+// (K=8; K=36 75.0 -> 43.8, with 20-40 bytes of scratch at 3 waves).  The
+// fp32 rows ran slower with the copy at 12 chunks (E=3072: 56.3 -> 58.1
+// us) and with 3 waves per SIMD at 9 (E=2304: 44.2 -> 47.5 us).
 template <int LPT, int NCH, typename TIn, int SCORE, int SEL, int GM, bool VEC,
           int WPB = kWaves>
 __global__ void __launch_bounds__(
     64 * WPB, GM == GROUP_LDS && VEC && NCH <= 4 ? 3
               : GM == GROUP_REG ? (NCH <= 2 && LPT >= 32 ? 5 : 4)
-              : (GM == GROUP_NONE && NCH == 16 && VEC && SCORE == SCORE_SIGMOID ? 2 : 1))
+              : GM != GROUP_NONE || !VEC ? 1
+              : NCH == 16 && SCORE == SCORE_SIGMOID ? 2
+              : (NCH == 9 || NCH == 12) && sizeof(TIn) == 2 ? 3 : 1)
 fwd_kernel(FwdParams p)
 {
     constexpr int GPW = 64 / LPT;            // token groups per wave
@@ -834,7 +841,7 @@ fwd_kernel(FwdParams p)
     for (int64_t tb = (int64_t)blockIdx.x * TPB; tb < p.T;
          tb += (int64_t)gridDim.x * TPB) {
         int lane = lane0;
-        if constexpr (NCH >= 16 || (NCH >= 12 && sizeof(TIn) == 2))
+        if constexpr (NCH >= 16 || (NCH >= 6 && sizeof(TIn) == 2))
             asm volatile("" : "+v"(lane));  // per iteration: see above
         const int j_lane = lane_part<VEC>(lane);
         const int64_t t0 = tb + wave * GPW;                // first token of the wave

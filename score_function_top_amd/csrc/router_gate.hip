@@ -8,9 +8,11 @@
 // shared_base + s in the columns after the K routed ones.  The maths is
 // stated in include/router.h.
 //
-// One wave per token (grid-stride over tokens).  The routed half is the
-// ordered top-K of router_topk_wave.h; a hidden row of up to 8 pieces per
-// lane is requested before it.  The gate half is a GEMV with S <= 16
+// shared_gate_kernel: one wave per token (grid-stride over tokens), its
+// hidden row of up to 8 pieces per lane requested before the routed half.
+// shared_gate_split_kernel, up to 1024 tokens: one wave per half of a
+// token.  The routed half is the ordered top-K of router_topk_wave.h.  The
+// gate half is a GEMV with S <= 16
 // outputs per token, bound by the hidden-state read (H elements per token,
 // S flops each): it runs on the VALU, not on matrix cores.  Lane l owns
 // the 16-byte pieces h = c*64*VH + VH*l (VH elements per piece); each piece
@@ -178,18 +180,173 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
     }
 }
 
-template <int NCH, typename TIn, bool PRE>
+// Up to this many tokens each token is two wave tasks of one launch, the
+// routed half and the gate half, which then run side by side (one round
+// of waves at these sizes, so the token's latency is the longer half, not
+// the sum: M = 1 4.0 -> 3.7 us, M = 256 4.6 -> 4.2 us on MI355X at E=512,
+// hidden 4096, bf16).  Above it one wave takes both halves of a token, its
+// hidden row requested before the routed half so that the row's latency
+// hides behind that work (M = 4096 10.7 us against 11.9 split, M = 16384
+// 30.9 against 32.5).
+constexpr int64_t kGateSplitMaxTokens = 1024;
+
+// The gate half over a prefetched hidden row: S dot products, each a wave
+// sum; lane K + s returns gate s.
+template <typename TIn, bool VEC_H>
+__device__ __forceinline__ float gate_prefetched(const GateParams &p, rsrc_t rgw,
+                                                 const uint32_t (&hpre)[kGatePrefetch][4], int lane)
+{
+    constexpr int VH = 16 / (int)io<TIn>::kSize;
+    const int H = p.H;
+    float gate = 0.0f;
+    for (int s = 0; s < p.S; s++) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kGatePrefetch; c++) {
+            const int h = c * 64 * VH + VH * lane;
+            uint32_t gv[4];
+            load16<TIn, VEC_H, 0>(rgw, s * H + h, s * H + H, gv);
+            acc = dot16<TIn>(hpre[c], gv, acc);
+        }
+        const float logit = group_sum<64>(acc);
+        // every lane evaluates it: no lane-divergent branch
+        const float sg = p.scale * sigmoid_fast(logit);
+        gate = lane == p.K + s ? sg : gate;
+    }
+    return gate;
+}
+
+// The gate half for longer rows: the hidden row streamed piece by piece
+// against all S gate rows.
+template <typename TIn, bool VEC_H>
+__device__ __forceinline__ float gate_streamed(const GateParams &p, rsrc_t rgw, rsrc_t rh,
+                                               int lane)
+{
+    constexpr int VH = 16 / (int)io<TIn>::kSize;
+    const int H = p.H, S = p.S;
+    const int pieces = (H + 64 * VH - 1) / (64 * VH);
+    float acc[kGateMaxShared];
+#pragma unroll
+    for (int s = 0; s < kGateMaxShared; s++)
+        acc[s] = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < pieces; c++) {
+        const int h = c * 64 * VH + VH * lane;
+        uint32_t hv[4];
+        load16<TIn, VEC_H, kStream>(rh, h, H, hv);
+#pragma unroll
+        for (int s = 0; s < kGateMaxShared; s++) {
+            if (s < S) {
+                uint32_t gv[4];
+                load16<TIn, VEC_H, 0>(rgw, s * H + h, s * H + H, gv);
+                acc[s] = dot16<TIn>(hv, gv, acc[s]);
+            }
+        }
+    }
+    float gate = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kGateMaxShared; s++) {
+        if (s < S) {
+            const float logit = group_sum<64>(acc[s]);
+            const float sg = p.scale * sigmoid_fast(logit);
+            gate = lane == p.K + s ? sg : gate;
+        }
+    }
+    return gate;
+}
+
+// The whole hidden row of token m (up to kGatePrefetch pieces per lane),
+// requested at once.
+template <typename TIn, bool VEC_H>
+__device__ __forceinline__ void prefetch_row(rsrc_t rh, int H, int lane,
+                                             uint32_t (&hpre)[kGatePrefetch][4])
+{
+    constexpr int VH = 16 / (int)io<TIn>::kSize;
+#pragma unroll
+    for (int c = 0; c < kGatePrefetch; c++)
+        load16<TIn, VEC_H, kStream>(rh, c * 64 * VH + VH * lane, H, hpre[c]);
+}
+
+// Row m's K routed slots (lane k < K) alone ...
+__device__ __forceinline__ void store_routed(const GateParams &p, int64_t m, int lane, int id,
+                                             float wt)
+{
+    const uint32_t nb = (uint32_t)(p.K + p.S) * 4u;
+    const rsrc_t rw = make_rsrc(p.weights + m * p.ld, nb);
+    const rsrc_t ri = make_rsrc(p.ids + m * p.ld, nb);
+    const uint32_t o = lane < p.K ? (uint32_t)lane * 4u : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b32(as_u(wt), rw, (int)o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)id, ri, (int)o, 0, 0);
+}
+
+// ... and its S gates (lane K + s) alone.
+__device__ __forceinline__ void store_gates(const GateParams &p, int64_t m, int lane, float gate)
+{
+    const uint32_t nb = (uint32_t)(p.K + p.S) * 4u;
+    const rsrc_t rw = make_rsrc(p.weights + m * p.ld, nb);
+    const rsrc_t ri = make_rsrc(p.ids + m * p.ld, nb);
+    const uint32_t o = lane >= p.K && lane < p.K + p.S ? (uint32_t)lane * 4u : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b32(as_u(gate), rw, (int)o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(p.base + (lane - p.K)), ri, (int)o, 0, 0);
+}
+
+// Grid-stride over 2*M wave tasks: task t is the routed half (t even) or
+// the gate half (t odd) of token t/2; the same arithmetic as
+// shared_gate_kernel, so the outputs are the same bit for bit.
+template <int NCH, typename TIn, bool VEC_G, bool VEC_H, bool PRE>
+__global__ __launch_bounds__(kBlock) void shared_gate_split_kernel(GateParams p)
+{
+    __shared__ uint64_t cand[kWaves][kSortedSlots];
+    constexpr uint32_t sz = io<TIn>::kSize;
+    const int lane = lane_id();
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    const int E = p.E, H = p.H;
+    const rsrc_t rgw = make_rsrc(p.gw, (uint32_t)p.S * (uint32_t)H * sz);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+
+    for (int64_t t = (int64_t)blockIdx.x * kWaves + wave; t < 2 * p.M; t += nwaves) {
+        const int64_t m = t >> 1;
+        if ((t & 1) == 0) {  // wave-uniform
+            const rsrc_t rx = make_rsrc((const char *)p.x + m * E * sz, (uint32_t)E * sz);
+            int id;
+            float wt;
+            wave_topk_row<NCH, TIn, VEC_G>(rx, E, p.K, SCORE_SOFTMAX, p.renorm, cand[wave], id,
+                                           wt);
+            store_routed(p, m, lane, id, wt);
+            continue;
+        }
+        const rsrc_t rh = make_rsrc((const char *)p.hs + m * H * sz, (uint32_t)H * sz);
+        float gate;
+        if constexpr (PRE) {
+            uint32_t hpre[kGatePrefetch][4];
+            prefetch_row<TIn, VEC_H>(rh, H, lane, hpre);
+            gate = gate_prefetched<TIn, VEC_H>(p, rgw, hpre, lane);
+        } else {
+            gate = gate_streamed<TIn, VEC_H>(p, rgw, rh, lane);
+        }
+        store_gates(p, m, lane, gate);
+    }
+}
+
+template <int NCH, typename TIn, bool PRE, bool SPLIT>
 hipError_t gate_p(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hipStream_t st)
 {
     const dim3 g(grid), b(kBlock);
-    if (vec_g && vec_h)
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, true, PRE>), g, b, 0, st, p);
-    else if (vec_g)
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, true, false, PRE>), g, b, 0, st, p);
-    else if (vec_h)
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, true, PRE>), g, b, 0, st, p);
-    else
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, false, false, PRE>), g, b, 0, st, p);
+#define ROUTER_GATE_LAUNCH(VG, VH)                                                           \
+    if constexpr (SPLIT)                                                                   \
+        hipLaunchKernelGGL((shared_gate_split_kernel<NCH, TIn, VG, VH, PRE>), g, b, 0, st, p); \
+    else                                                                                   \
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, VG, VH, PRE>), g, b, 0, st, p);
+    if (vec_g && vec_h) {
+        ROUTER_GATE_LAUNCH(true, true)
+    } else if (vec_g) {
+        ROUTER_GATE_LAUNCH(true, false)
+    } else if (vec_h) {
+        ROUTER_GATE_LAUNCH(false, true)
+    } else {
+        ROUTER_GATE_LAUNCH(false, false)
+    }
+#undef ROUTER_GATE_LAUNCH
     return hipGetLastError();
 }
 
@@ -198,8 +355,11 @@ hipError_t gate_t(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hi
 {
     const int vh = 16 / (int)sizeof(TIn);
     const bool pre = vec_h && p.H <= kGatePrefetch * 64 * vh;
-    return pre ? gate_p<NCH, TIn, true>(p, vec_g, vec_h, grid, st)
-               : gate_p<NCH, TIn, false>(p, vec_g, vec_h, grid, st);
+    if (p.M <= kGateSplitMaxTokens)
+        return pre ? gate_p<NCH, TIn, true, true>(p, vec_g, vec_h, grid, st)
+                   : gate_p<NCH, TIn, false, true>(p, vec_g, vec_h, grid, st);
+    return pre ? gate_p<NCH, TIn, true, false>(p, vec_g, vec_h, grid, st)
+               : gate_p<NCH, TIn, false, false>(p, vec_g, vec_h, grid, st);
 }
 
 template <int NCH>
@@ -217,7 +377,8 @@ hipError_t launch_shared_gate(const GateParams &p, int dtype, bool vec_g, bool v
 {
     if (p.M == 0)
         return hipSuccess;
-    const int64_t blocks = (p.M + kWaves - 1) / kWaves;
+    const int64_t ntask = p.M <= kGateSplitMaxTokens ? 2 * p.M : p.M;  // wave tasks
+    const int64_t blocks = (ntask + kWaves - 1) / kWaves;
     const unsigned grid = (unsigned)(blocks < kGateMaxBlocks ? blocks : kGateMaxBlocks);
     if (p.E <= 256)
         return gate_nch<1>(p, dtype, vec_g, vec_h, grid, stream);

@@ -9,7 +9,8 @@
 // stated in include/router.h.
 //
 // shared_gate_kernel: one wave per token (grid-stride over tokens), its
-// hidden row of up to 8 pieces per lane requested before the routed half.
+// hidden row of up to 8 pieces per lane requested before the routed half
+// (from 8192 tokens on, every load first and the routed half last).
 // shared_gate_split_kernel, up to 1024 tokens: one wave per half of a
 // token.  The routed half is the ordered top-K of router_topk_wave.h.  The
 // gate half is a GEMV with S <= 16
@@ -98,7 +99,15 @@ __device__ __forceinline__ void store_row(const GateParams &p, int64_t m, int la
 // when the whole row fits: 4096 bf16 or 2048 fp32 elements.
 constexpr int kGatePrefetch = 8;
 
-template <int NCH, typename TIn, bool VEC_G, bool VEC_H, bool PRE>
+// LATE (prefetched rows only): every load of the token first -- hidden row,
+// the first gate row, gating row -- then the gate half, then the routed
+// half on the loaded logits; nothing is held across the routed half (103
+// VGPRs against 119 at E=512, bf16).  From two rounds of waves on, other
+// waves' loads cover the routed half at the end (on MI355X at E=512,
+// hidden 4096: M = 8192 the same within 1%, M = 12288 24.7 -> 24.4 us,
+// M = 16384 31.2 -> 30.2); in a single round nothing does (M = 4096
+// 10.5 -> 10.6, M = 6144 14.4 -> 15.2).
+template <int NCH, typename TIn, bool VEC_G, bool VEC_H, bool PRE, bool LATE = false>
 __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
 {
     __shared__ uint64_t cand[kWaves][kSortedSlots];
@@ -113,6 +122,43 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
 
     for (int64_t m = (int64_t)blockIdx.x * kWaves + wave; m < p.M; m += nwaves) {
         const rsrc_t rh = make_rsrc((const char *)p.hs + m * H * sz, (uint32_t)H * sz);
+        if constexpr (PRE && LATE) {
+            const rsrc_t rx = make_rsrc((const char *)p.x + m * E * sz, (uint32_t)E * sz);
+            uint32_t hrow[kGatePrefetch][4], g0[kGatePrefetch][4];
+#pragma unroll
+            for (int c = 0; c < kGatePrefetch; c++)
+                load16<TIn, VEC_H, kStream>(rh, c * 64 * VH + VH * lane, H, hrow[c]);
+#pragma unroll
+            for (int c = 0; c < kGatePrefetch; c++)
+                load16<TIn, VEC_H, 0>(rgw, c * 64 * VH + VH * lane, H, g0[c]);
+            float key[NCH][4];
+            wave_topk_load<NCH, TIn, VEC_G>(rx, E, key);
+            float gate = 0.0f;
+            for (int s = 0; s < S; s++) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int c = 0; c < kGatePrefetch; c++) {
+                    const int h = c * 64 * VH + VH * lane;
+                    uint32_t gv[4];
+                    if (s == 0) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++)
+                            gv[q] = g0[c][q];
+                    } else {
+                        load16<TIn, VEC_H, 0>(rgw, s * H + h, s * H + H, gv);
+                    }
+                    acc = dot16<TIn>(hrow[c], gv, acc);
+                }
+                const float logit = group_sum<64>(acc);
+                const float sg = p.scale * sigmoid_fast(logit);
+                gate = lane == K + s ? sg : gate;
+            }
+            int id;
+            float wt;
+            wave_topk_keys<NCH>(key, K, SCORE_SOFTMAX, p.renorm, cand[wave], id, wt);
+            store_row(p, m, lane, id, wt, gate);
+            continue;
+        }
         [[maybe_unused]] uint32_t hpre[kGatePrefetch][4];
         if constexpr (PRE) {
             // the whole hidden row is requested before the routed half, so
@@ -189,6 +235,10 @@ __global__ __launch_bounds__(kBlock) void shared_gate_kernel(GateParams p)
 // hides behind that work (M = 4096 10.7 us against 11.9 split, M = 16384
 // 30.9 against 32.5).
 constexpr int64_t kGateSplitMaxTokens = 1024;
+// From this many tokens (two rounds of resident waves at E=512, bf16) the
+// prefetched-row kernel takes its routed half last (shared_gate_kernel,
+// LATE).
+constexpr int64_t kGateLateMinTokens = 8192;
 
 // The gate half over a prefetched hidden row: S dot products, each a wave
 // sum; lane K + s returns gate s.
@@ -328,15 +378,20 @@ __global__ __launch_bounds__(kBlock) void shared_gate_split_kernel(GateParams p)
     }
 }
 
-template <int NCH, typename TIn, bool PRE, bool SPLIT>
+// Launch modes: one wave per token, the same with the routed half last
+// (LATE), one wave per half of a token (split kernel).
+enum GateMode { kGateFused, kGateLate, kGateSplit };
+
+template <int NCH, typename TIn, bool PRE, int MODE>
 hipError_t gate_p(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hipStream_t st)
 {
     const dim3 g(grid), b(kBlock);
-#define ROUTER_GATE_LAUNCH(VG, VH)                                                           \
-    if constexpr (SPLIT)                                                                   \
-        hipLaunchKernelGGL((shared_gate_split_kernel<NCH, TIn, VG, VH, PRE>), g, b, 0, st, p); \
-    else                                                                                   \
-        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, VG, VH, PRE>), g, b, 0, st, p);
+#define ROUTER_GATE_LAUNCH(VG, VH)                                                             \
+    if constexpr (MODE == kGateSplit)                                                        \
+        hipLaunchKernelGGL((shared_gate_split_kernel<NCH, TIn, VG, VH, PRE>), g, b, 0, st, p);   \
+    else                                                                                     \
+        hipLaunchKernelGGL((shared_gate_kernel<NCH, TIn, VG, VH, PRE, MODE == kGateLate>), g, b, \
+                           0, st, p);
     if (vec_g && vec_h) {
         ROUTER_GATE_LAUNCH(true, true)
     } else if (vec_g) {
@@ -356,10 +411,12 @@ hipError_t gate_t(const GateParams &p, bool vec_g, bool vec_h, unsigned grid, hi
     const int vh = 16 / (int)sizeof(TIn);
     const bool pre = vec_h && p.H <= kGatePrefetch * 64 * vh;
     if (p.M <= kGateSplitMaxTokens)
-        return pre ? gate_p<NCH, TIn, true, true>(p, vec_g, vec_h, grid, st)
-                   : gate_p<NCH, TIn, false, true>(p, vec_g, vec_h, grid, st);
-    return pre ? gate_p<NCH, TIn, true, false>(p, vec_g, vec_h, grid, st)
-               : gate_p<NCH, TIn, false, false>(p, vec_g, vec_h, grid, st);
+        return pre ? gate_p<NCH, TIn, true, kGateSplit>(p, vec_g, vec_h, grid, st)
+                   : gate_p<NCH, TIn, false, kGateSplit>(p, vec_g, vec_h, grid, st);
+    if (pre && p.M >= kGateLateMinTokens)
+        return gate_p<NCH, TIn, true, kGateLate>(p, vec_g, vec_h, grid, st);
+    return pre ? gate_p<NCH, TIn, true, kGateFused>(p, vec_g, vec_h, grid, st)
+               : gate_p<NCH, TIn, false, kGateFused>(p, vec_g, vec_h, grid, st);
 }
 
 template <int NCH>

@@ -77,13 +77,13 @@ __device__ __forceinline__ bool sorted_topk(const float (&key)[NCH][4], int K, u
     return true;
 }
 
+// A row of E logits, 4 per lane and chunk (element c*256 + 4*lane + u),
+// -inf past E.
 template <int NCH, typename TIn, bool VEC, int POL = kStream>
-__device__ __forceinline__ void wave_topk_row(rsrc_t r, int E, int K, int score, int renorm,
-                                              uint64_t *cand, int &my_id, float &my_w)
+__device__ __forceinline__ void wave_topk_load(rsrc_t r, int E, float (&key)[NCH][4])
 {
     const int lane = lane_id();
     constexpr uint32_t sz = io<TIn>::kSize;
-    float key[NCH][4];
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
         const int j0 = c * 256 + 4 * lane;
@@ -101,6 +101,15 @@ __device__ __forceinline__ void wave_topk_row(rsrc_t r, int E, int K, int score,
             }
         }
     }
+}
+
+// The ordered top-K of a loaded row: lane k < K gets slot k's expert and
+// weight.
+template <int NCH>
+__device__ __forceinline__ void wave_topk_keys(float (&key)[NCH][4], int K, int score, int renorm,
+                                               uint64_t *cand, int &my_id, float &my_w)
+{
+    const int lane = lane_id();
     float mx = 0.0f, rz = 0.0f;
     if (score == SCORE_SOFTMAX) {
         float m = -INFINITY;
@@ -190,6 +199,16 @@ __device__ __forceinline__ void wave_topk_row(rsrc_t r, int E, int K, int score,
             den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
         my_w = my_s / den;
     }
+}
+
+// Both: load the row, then select.
+template <int NCH, typename TIn, bool VEC, int POL = kStream>
+__device__ __forceinline__ void wave_topk_row(rsrc_t r, int E, int K, int score, int renorm,
+                                              uint64_t *cand, int &my_id, float &my_w)
+{
+    float key[NCH][4];
+    wave_topk_load<NCH, TIn, VEC, POL>(r, E, key);
+    wave_topk_keys<NCH>(key, K, score, renorm, cand, my_id, my_w);
 }
 
 }  // namespace rker

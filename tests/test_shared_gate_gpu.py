@@ -87,8 +87,21 @@ def test_page_axes_and_edges(kw):
     run(**a)
 
 
-# The library takes one wave per half of a token up to 1024 tokens and one
-# wave per token above; the edges again on the second kernel.
+# The library takes one wave per half of a token up to 1024 tokens, one
+# wave per token above, and from 8192 tokens on (rows that fit the
+# prefetch) one wave per token with the routed half last; the edges again
+# on the last two.
+_LATE_EDGES = [dict(), dict(S=8), dict(dtype=synth.F32), dict(renorm=False, scale=0.5),
+               dict(E=1000, K=32, S=16), dict(ld_extra=5), dict(ties=True, K=32), dict(K=3)]
+
+
+@pytest.mark.parametrize("kw", _LATE_EDGES)
+def test_page_axes_and_edges_routed_half_last(kw):
+    a = dict(M=8200, E=512, H=4096, K=10, S=1)
+    a.update(kw)
+    run(**a)
+
+
 @pytest.mark.parametrize("kw", [
     dict(), dict(S=8), dict(dtype=synth.F32), dict(renorm=False, scale=0.5),
     dict(E=1000, K=32, S=16), dict(H=4100), dict(H=33, dtype=synth.F32), dict(H=7168),
@@ -100,20 +113,23 @@ def test_page_axes_and_edges_many_tokens(kw):
     run(**a)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(E=1000, K=32, S=16, H=4100, dtype=synth.F32),
+@pytest.mark.parametrize("m_big,m_small", [(1100, 1024), (8200, 8000)])
+@pytest.mark.parametrize("kw", [dict(), dict(E=1000, K=32, S=16, dtype=synth.F32),
+                                dict(E=1000, K=32, S=16, H=4100, dtype=synth.F32),
                                 dict(ties=True, K=32), dict(H=7168, S=2)])
-def test_split_and_fused_kernels_agree(kw):
-    """The first 1024 rows of a 1100-token call (one wave per token) equal,
-    bit for bit, the call on those 1024 rows alone (one wave per half)."""
+def test_gate_kernels_agree(kw, m_big, m_small):
+    """The first rows of a longer call equal, bit for bit, the call on those
+    rows alone: 1100 tokens (one wave per token) against 1024 (one wave per
+    half), 8200 (routed half last) against 8000 (routed half first)."""
     a = dict(E=512, H=4096, K=10, S=1, dtype=synth.BF16, ties=False)
     a.update(kw)
-    say(f"[shared gate] split vs fused {a}")
-    (xt, ht, gt), _ = inputs(9650, 1100, a["E"], a["H"], a["S"], a["dtype"], ties=a["ties"])
+    say(f"[shared gate] {m_big} against {m_small} tokens {a}")
+    (xt, ht, gt), _ = inputs(9650, m_big, a["E"], a["H"], a["S"], a["dtype"], ties=a["ties"])
     w1, i1 = router.router_topk_shared_gate(xt, ht, gt, a["K"])
-    w0, i0 = router.router_topk_shared_gate(xt[:1024], ht[:1024], gt, a["K"])
+    w0, i0 = router.router_topk_shared_gate(xt[:m_small], ht[:m_small], gt, a["K"])
     torch.cuda.synchronize()
-    assert torch.equal(i0, i1[:1024])
-    assert torch.equal(w0.view(torch.int32), w1[:1024].view(torch.int32))
+    assert torch.equal(i0, i1[:m_small])
+    assert torch.equal(w0.view(torch.int32), w1[:m_small].view(torch.int32))
 
 
 def test_zero_tokens_noop():

@@ -72,10 +72,12 @@ _GATE_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_par
                  "router_topk_wave.h", "router_gate.hip"]
 _GROUPED_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_kernels.h",
                     "router_params.h", "router_grouped.h", "router_grouped.hip"]
+_ROUTE_SOURCES = ["router_api.cpp", "router_device.h", "router_io.h", "router_params.h",
+                  "router_topk_wave.h", "router_route.hip"]
 SYMBOL_SOURCES = {"fwd_kernel": _ROUTER_SOURCES, "bwd_kernel": _ROUTER_SOURCES,
                   "loss_kernel": _LOSS_SOURCES, "count_kernel": _LOSS_SOURCES,
                   "loss_bwd_kernel": _LOSS_SOURCES, "shared_gate_kernel": _GATE_SOURCES,
-                  "grouped_fwd_kernel": _GROUPED_SOURCES}
+                  "grouped_fwd_kernel": _GROUPED_SOURCES, "route_maps_kernel": _ROUTE_SOURCES}
 
 
 def path_threshold_desc(router):
@@ -929,7 +931,8 @@ def main():
         "kernel_source_hash": {"router": kernel_source_hash("fwd_kernel"),
                                "loss": kernel_source_hash("loss_kernel"),
                                "gate": kernel_source_hash("shared_gate_kernel"),
-                               "grouped": kernel_source_hash("grouped_fwd_kernel")},
+                               "grouped": kernel_source_hash("grouped_fwd_kernel"),
+                               "route": kernel_source_hash("route_maps_kernel")},
     }
     if not args.only:
         loss = {}

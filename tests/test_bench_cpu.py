@@ -60,7 +60,8 @@ def test_hash_sources_cover_the_build():
     router_units = {f for f in built if re.match(r"router_(lpt\d+\w*|scalar\d*)\.hip$", f)}
     assert router_units and router_units <= set(bench._ROUTER_SOURCES)
     for unit, sym in (("router_loss.hip", "loss_kernel"), ("router_gate.hip", "shared_gate_kernel"),
-                      ("router_grouped.hip", "grouped_fwd_kernel")):
+                      ("router_grouped.hip", "grouped_fwd_kernel"),
+                      ("router_route.hip", "route_maps_kernel")):
         assert unit in bench.SYMBOL_SOURCES[sym]
     # headers every kernel unit includes
     for sym in bench.SYMBOL_SOURCES:
